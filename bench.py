@@ -1,0 +1,294 @@
+"""Benchmark of the weight-streaming skinny GEMM on one MI355X.
+
+One step = one pass of the hot path over one batch: the NVFP4 GEMMs of one
+MLP block of a ~27B dense decoder at M=1 (gate_up 34816x5120 then down
+5120x17408), every weight read from HBM in its packed form. Weights live in
+enough distinct copies (>= 2 GiB) that no launch finds its matrix in the
+256 MB last-level cache; inputs are resident in HBM before timing starts.
+
+Prints one JSON line. ``value`` is the effective HBM read bandwidth of the
+step (algorithmic bytes: packed codes + block scales + x + y, divided by the
+step time). Also reported: the read-only streaming ceiling measured in the
+same run, per-matrix times for M=1 and M=8 (and FP8 M=1,2,4 and the full
+64-layer decode step with --all), the roofline of the dominant kernel, and
+the CPU oracle timed on a bounded sample (baseline only).
+"""
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "effective HBM read GB/s (% of ceiling), NVFP4/FP8 skinny GEMM at M=1 and M=8"
+PEAK_HBM_GBPS = 8000.0
+ROTATE_BYTES = 2.5e9
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--all", action="store_true", help="also FP8 M=1,2,4 and the 64-layer decode step")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="only the headline step")
+    p.add_argument("--cpu-rows", type=int, default=1024, help="rows per matrix in the CPU oracle sample")
+    return p.parse_args()
+
+
+class Mat:
+    """One packed weight in R rotating device copies."""
+
+    def __init__(self, name, fmt, wl, copies=None):
+        import torch
+        from quantized_weight_skinny_amd import torch_api as qt
+        self.name, self.fmt = name, fmt
+        n, k = workloads.SHAPES[name]
+        self.n, self.k = n, k
+        w = workloads.weights(n, k, workloads.seed_for(wl, name, "W"))
+        wd = torch.from_numpy(w).to("cuda")
+        del w
+        if fmt == "nvfp4":
+            codes, scales, s_t = qt.quantize_nvfp4(wd)
+            pw = qt.pack_nvfp4(codes, scales, s_t, n, k)
+            del codes, scales
+        else:
+            codes, rs = qt.quantize_fp8(wd)
+            pw = qt.pack_fp8(codes, rs, n, k)
+            del codes
+        del wd
+        self.weight_bytes = pw.nbytes
+        r = copies or max(1, int(np.ceil(ROTATE_BYTES / self.weight_bytes)))
+        self.copies = [pw]
+        for _ in range(r - 1):
+            rs = pw.row_scales.clone() if pw.row_scales is not None else None
+            self.copies.append(qt.PackedWeight(pw.fmt, n, k, pw.packed.clone(), pw.tensor_scale, rs))
+        torch.cuda.synchronize()
+
+    def bytes_for(self, m):
+        return self.weight_bytes + 2 * m * self.k + 2 * m * self.n
+
+
+def time_matrix(mat, m, iters, warm=5):
+    """Average µs per launch of one matrix, back to back over rotating copies,
+    timed with events on the launch stream."""
+    import torch
+    from quantized_weight_skinny_amd import torch_api as qt
+    x = torch.randn((m, mat.k), device="cuda").half()
+    y = torch.empty((m, mat.n), dtype=torch.float16, device="cuda")
+    ws_need = max(qt.workspace_bytes(c, m) for c in mat.copies[:1])
+    ws = torch.empty(max(ws_need, 16), dtype=torch.uint8, device="cuda")
+    r = len(mat.copies)
+    for i in range(warm):
+        qt.gemm(x, mat.copies[i % r], out=y, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(iters):
+        qt.gemm(x, mat.copies[i % r], out=y, workspace=ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    return us, mat.bytes_for(m) / (us * 1e-6) / 1e9
+
+
+def read_ceiling(nbytes=4 << 30, reps=8):
+    """Best read-only streaming bandwidth over a few grid sizes (GB/s)."""
+    import torch
+    from quantized_weight_skinny_amd import torch_api as qt
+    from quantized_weight_skinny_amd import qpn_read_ceiling_grid
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    base = qpn_read_ceiling_grid()
+    best = (0.0, 0)
+    for grid in (base // 4, base // 2, base, base * 2):
+        sink = torch.empty(grid * 4, dtype=torch.int32, device="cuda")
+        qt.read_ceiling(buf, grid, sink)
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            qt.read_ceiling(buf, grid, sink)
+        e1.record(s)
+        torch.cuda.synchronize()
+        gbps = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if gbps > best[0]:
+            best = (gbps, grid)
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
+def cpu_baseline(rows):
+    """The oracle (numpy, float64 dequantize then matmul) on a bounded sample:
+    the first ``rows`` rows of gate_up and of down at M=1, repeated to about
+    10 s of CPU time. GB/s over the same algorithmic bytes as the GPU step."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = 1
+    parts = []
+    for name in ("gate_up", "down"):
+        n, k = workloads.SHAPES[name]
+        w = workloads.weights(n, k, workloads.seed_for("nvfp4_27b_m1", name, "W"), rows=slice(0, rows))
+        full_amax = None  # the sample is quantized on its own; timing does not depend on values
+        codes, sc, s_t = oracle.quantize_nvfp4(w, full_amax)
+        x = workloads.activations(1, k, workloads.seed_for("nvfp4_27b_m1", name, "x"))
+        nbytes = rows * k // 2 + rows * k // 16 + 2 * k + 2 * rows
+        parts.append((codes, sc, s_t, x, nbytes))
+    total_bytes = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for codes, sc, s_t, x, nbytes in parts:
+            oracle.gemm_nvfp4(x, codes, sc, s_t)
+            total_bytes += nbytes
+        reps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": total_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} rows of gate_up and of down (NVFP4, M=1), numpy float64 dequantize + "
+                      f"matmul, {reps} passes in {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU (--gpus > 1) is not "
+                                   "part of this build", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    from quantized_weight_skinny_amd import torch_api as qt  # noqa: F401  (fails loudly without libqpn.so)
+
+    log("read ceiling")
+    ceiling, ceiling_grid = read_ceiling()
+    log(f"ceiling {ceiling:.0f} GB/s (grid {ceiling_grid})")
+
+    log("building rotating weights for the M=1 MLP step")
+    wl = "nvfp4_27b_m1"
+    gate_up = Mat("gate_up", "nvfp4", wl)
+    r_steps = len(gate_up.copies)
+    down = Mat("down", "nvfp4", wl, copies=r_steps)
+    m = 1
+    x1 = torch.randn((m, 5120), device="cuda").half()
+    x2 = torch.randn((m, 17408), device="cuda").half()
+    h = torch.empty((m, 34816), dtype=torch.float16, device="cuda")
+    y = torch.empty((m, 5120), dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(qt.workspace_bytes(down.copies[0], m), 16), dtype=torch.uint8, device="cuda")
+    step_bytes = gate_up.bytes_for(m) + down.bytes_for(m)
+
+    def step(i):
+        qt.gemm(x1, gate_up.copies[i % r_steps], out=h)
+        qt.gemm(x2, down.copies[i % r_steps], out=y, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(s)
+    for i in range(args.steps):
+        ev[i][0].record(s)
+        qt.gemm(x1, gate_up.copies[i % r_steps], out=h)  # the dominant kernel, timed per launch
+        ev[i][1].record(s)
+        qt.gemm(x2, down.copies[i % r_steps], out=y, workspace=ws)
+    t1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    gate_up_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = gate_up.bytes_for(m) / (gate_up_us * 1e-6) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us, {value:.0f} GB/s; gate_up {gate_up_us:.1f} us {achieved:.0f} GB/s; "
+        f"wall {wall:.2f} s")
+
+    extras = {}
+    if not args.no_extras:
+        per = {}
+        per["nvfp4_m1/gate_up"] = time_matrix(gate_up, 1, 40)
+        per["nvfp4_m1/down"] = time_matrix(down, 1, 40)
+        per["nvfp4_m8/gate_up"] = time_matrix(gate_up, 8, 40)
+        per["nvfp4_m8/down"] = time_matrix(down, 8, 40)
+        del gate_up, down
+        torch.cuda.empty_cache()
+        for name in ("qkv", "o_proj"):
+            mat = Mat(name, "nvfp4", "nvfp4_27b_m8")
+            per[f"nvfp4_m8/{name}"] = time_matrix(mat, 8, 60)
+            del mat
+            torch.cuda.empty_cache()
+        if args.all:
+            for name in ("qkv", "down"):
+                mat = Mat(name, "fp8", "fp8_27b_m124")
+                for mm in (1, 2, 4):
+                    per[f"fp8_m{mm}/{name}"] = time_matrix(mat, mm, 60)
+                del mat
+                torch.cuda.empty_cache()
+        for key, (us, gbps) in per.items():
+            extras[key] = {"us": round(us, 2), "GBps": round(gbps, 1),
+                           "frac_of_measured_ceiling": round(gbps / ceiling, 4)}
+            log(f"{key}: {us:.1f} us {gbps:.0f} GB/s ({100 * gbps / ceiling:.1f}% of ceiling)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(args.cpu_rows)
+        log(f"cpu baseline {cpu['value']:.3f} GB/s")
+
+    try:
+        sha = subprocess.run(["git", "rev-parse", "--short", "HEAD"], capture_output=True, text=True,
+                             cwd=ROOT).stdout.strip() or None
+    except Exception:
+        sha = None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "nvfp4_27b_m1: NVFP4 gate_up 34816x5120 + down 5120x17408, M=1",
+                   "m": 1, "format": "nvfp4", "rotating_copies": r_steps, "step_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "gemm_kernel<NVFP4> on gate_up 34816x5120, M=1"},
+        "measured_read_ceiling_GBps": round(ceiling, 1),
+        "frac_of_measured_ceiling": round(value / ceiling, 4),
+        "cpu_baseline": cpu,
+        "per_matrix": extras,
+        "git": sha,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * qpn.h - C ABI of libqpn.so, a weight-streaming skinny GEMM for AMD MI355X
+ * (gfx950): y[M, N] = x[M, K] * dequant(W)^T with M = 1..16 fp16 activation
+ * rows and W held compressed in HBM as NVFP4 or FP8 (E4M3), decoded to fp16
+ * in registers right before the matrix-core multiply.
+ *
+ * Pages cited ([P3]): https://reddlx.com/feed/productivity-ai-news, the post
+ * "Four Tesla V100s from 2017 matched my RTX 5090 on single-request Qwen 3.8
+ * decode"; section names are that post's headings.
+ *
+ * Conventions for every entry point:
+ *   - All pointers named *_dev are device pointers (hipMalloc'd, or torch CUDA
+ *     tensors); the caller owns every buffer. The library allocates no memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Device work is
+ *     enqueued on it and the call returns without waiting, unless stated.
+ *   - Arguments are validated on the host before any HIP call; a failed check
+ *     returns a negative qpn_status and enqueues nothing. A failed kernel
+ *     launch returns QPN_ERR_HIP. Faults inside kernels surface
+ *     asynchronously, as HIP reports them.
+ *   - No global mutable state: calls may run concurrently on different
+ *     streams as long as their output buffers do not overlap.
+ */
+#ifndef QPN_H
+#define QPN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QPN_OK = 0,
+  QPN_ERR_INVALID_ARG = -1,      /* null / misaligned pointer, bad size or format */
+  QPN_ERR_UNSUPPORTED = -2,      /* valid request this build does not implement  */
+  QPN_ERR_BAD_CODE = -3,         /* reserved: invalid codes are counted, see pack */
+  QPN_ERR_BUFFER_TOO_SMALL = -4, /* packed buffer or workspace below the required size */
+  QPN_ERR_HIP = -5               /* a HIP runtime call failed */
+} qpn_status;
+
+typedef enum { QPN_FMT_NVFP4 = 1, QPN_FMT_FP8_E4M3 = 2 } qpn_format;
+
+/* Largest number of activation rows per call. A k-step speculative verify
+ * round multiplies k+1 rows (k=7 gives the 8 rows of [P3] "What I actually
+ * built"); the 16-row matrix-core tile holds up to 16 at no extra cost. */
+#define QPN_MAX_M 16
+
+/*
+ * A packed weight matrix W[N, K] as qpn_gemm reads it.
+ *   format       QPN_FMT_NVFP4 or QPN_FMT_FP8_E4M3.
+ *   n, k         logical shape; n >= 0, k >= 0, k % 16 == 0.
+ *   packed       device buffer written by qpn_pack_nvfp4 / qpn_pack_fp8 for
+ *                the same (format, n, k); 16-byte aligned; opaque layout.
+ *   tensor_scale NVFP4: the fp32 per-tensor scale s_t (host value). FP8: unused.
+ *   row_scales   FP8: device float[n], the fp32 scale of each output row.
+ *                NVFP4: unused (may be NULL).
+ * The value of element (n, k) is
+ *   NVFP4: E2M1(code[n][k]) * E4M3(block_scale[n][k / 16]) * tensor_scale
+ *   FP8:   E4M3(code[n][k]) * row_scales[n]
+ */
+typedef struct {
+  int32_t format;
+  int32_t reserved; /* must be 0 */
+  int64_t n;
+  int64_t k;
+  const void* packed;
+  float tensor_scale;
+  const float* row_scales;
+} qpn_weight;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* qpn_status_string(qpn_status s);
+
+/* Bytes of device memory the packed form of an [n, k] matrix occupies, or 0
+ * when the arguments are invalid (unknown format, n < 0, k < 0, k % 16 != 0).
+ * The packed form pads n up to a multiple of 16 and k up to a multiple of 256
+ * with zero weights. */
+size_t qpn_packed_bytes(int32_t format, int64_t n, int64_t k);
+
+/*
+ * Canonical NVFP4 -> packed device layout.
+ *   codes_dev        uint8 [n][k/2] row-major; byte j of a row holds element
+ *                    2j in its low nibble and 2j+1 in its high nibble (E2M1
+ *                    codes s|e1e0|m, OCP MX v1.0).
+ *   block_scales_dev uint8 [n][k/16] row-major E4M3FN codes, one per 16
+ *                    consecutive elements of a row along k.
+ *   packed_dev       output, packed_bytes >= qpn_packed_bytes(NVFP4, n, k),
+ *                    16-byte aligned. Every byte of the packed form is written.
+ *   bad_codes_dev    NULL, or a device int32 to which the kernel adds the
+ *                    number of NaN block-scale codes (0x7F / 0xFF) it found;
+ *                    the caller zeroes it first and checks it after the stream
+ *                    is synchronized. NaN scales make their block's outputs
+ *                    NaN; they never make the GEMM fault.
+ * The pages keep published FP4 regions in their own format rather than
+ * converting them ([P3] "v1.0 got us here. v1.1 removes its last
+ * compromise."); this entry point takes such codes as they are.
+ */
+qpn_status qpn_pack_nvfp4(const uint8_t* codes_dev, const uint8_t* block_scales_dev,
+                          int64_t n, int64_t k, void* packed_dev, size_t packed_bytes,
+                          int32_t* bad_codes_dev, void* stream);
+
+/* Canonical FP8 -> packed layout. codes_dev: uint8 [n][k] row-major E4M3FN
+ * codes. bad_codes_dev as for qpn_pack_nvfp4 (counts 0x7F / 0xFF codes).
+ * The per-row fp32 scales stay in a separate caller-owned array. ([P3] "v1.0
+ * got us here. v1.1 removes its last compromise.": FP8 regions keep FP8.) */
+qpn_status qpn_pack_fp8(const uint8_t* codes_dev, int64_t n, int64_t k,
+                        void* packed_dev, size_t packed_bytes,
+                        int32_t* bad_codes_dev, void* stream);
+
+/* Packed -> canonical (the inverse of the two pack calls, for round-trip
+ * checks). Outputs have the canonical shapes described above. */
+qpn_status qpn_unpack_nvfp4(const void* packed_dev, size_t packed_bytes, int64_t n, int64_t k,
+                            uint8_t* codes_dev, uint8_t* block_scales_dev, void* stream);
+qpn_status qpn_unpack_fp8(const void* packed_dev, size_t packed_bytes, int64_t n, int64_t k,
+                          uint8_t* codes_dev, void* stream);
+
+/*
+ * Synthetic-weight quantizers (offline helpers; the pages serve an already
+ * quantized checkpoint and do not give a recipe, so the plainest two-level
+ * one is used). All arithmetic is fp32, correctly rounded, ties to even.
+ *
+ * qpn_absmax_f32: out_dev[0] = max |x_dev[i]| over count floats (0 for
+ *   count == 0; NaN if any element is NaN). Deterministic.
+ * qpn_nvfp4_tensor_scale: host helper, amax / 2688 (= 6 * 448) in fp32, or 1
+ *   when that is zero.
+ * qpn_quantize_nvfp4: w_dev float [n][k] (finite; k % 16 == 0) and the
+ *   tensor scale s_t -> codes_dev uint8 [n][k/2] (canonical nibble order) and
+ *   block_scales_dev uint8 [n][k/16]:
+ *     sc = E4M3((amax_block / 6) / s_t); d = E4M3value(sc) * s_t;
+ *     code = d == 0 ? sign-only zero : E2M1(w / d), saturating at 6.
+ * qpn_quantize_fp8: w_dev float [n][k] (finite) -> codes_dev uint8 [n][k]
+ *   and row_scales_dev float [n]: s = amax_row / 448 (1 when zero),
+ *   code = E4M3(w / s), saturating at 448.
+ * Non-finite weights give unspecified codes (never a fault).
+ */
+qpn_status qpn_absmax_f32(const float* x_dev, int64_t count, float* out_dev, void* stream);
+float qpn_nvfp4_tensor_scale(float amax);
+qpn_status qpn_quantize_nvfp4(const float* w_dev, int64_t n, int64_t k, float tensor_scale,
+                              uint8_t* codes_dev, uint8_t* block_scales_dev, void* stream);
+qpn_status qpn_quantize_fp8(const float* w_dev, int64_t n, int64_t k,
+                            uint8_t* codes_dev, float* row_scales_dev, void* stream);
+
+/* Device workspace qpn_gemm needs for this weight and row count (0 if none). */
+size_t qpn_workspace_bytes(const qpn_weight* w, int32_t m);
+
+/*
+ * The hot path ([P3] "What I actually built": weights stay compressed while
+ * they stream from HBM and each fragment becomes fp16 in registers, with no
+ * dequantize-to-fp16 pass).
+ *   x_dev     fp16 [m][w->k] row-major, 16-byte aligned.
+ *   y_dev     fp16 [m][w->n] row-major output (fully overwritten), 2-byte aligned.
+ *   m         0..QPN_MAX_M activation rows (0 or n == 0: nothing to do).
+ *   workspace device scratch of at least qpn_workspace_bytes(w, m) bytes
+ *             (NULL allowed when that is 0); 16-byte aligned.
+ * Accumulation is fp32 over exactly decoded fp16 weights; the result is
+ * rounded once to fp16. Deterministic: the same inputs give the same bits.
+ * Never synchronizes the stream.
+ */
+qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
+                    void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * qpn_gemm with an explicit launch shape, for tuning sweeps: split_k > 0
+ * splits K into that many ranges (0 = choose automatically) and
+ * waves_per_group is 4 or 8 (0 = automatic). The workspace needed for an
+ * explicit split is qpn_workspace_bytes_split(w, m, split_k).
+ */
+qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
+                          void* workspace_dev, size_t workspace_bytes,
+                          int32_t split_k, int32_t waves_per_group, void* stream);
+size_t qpn_workspace_bytes_split(const qpn_weight* w, int32_t m, int32_t split_k);
+
+/*
+ * Read-only streaming kernel that measures the HBM read ceiling the GEMM is
+ * compared against ([P3] "What I actually built": bandwidth is quoted against
+ * a measured read-only ceiling). Reads `bytes` (a multiple of 16) from buf_dev
+ * with 16-byte loads on `grid` workgroups of 256 threads (grid 0 = automatic;
+ * qpn_read_ceiling_grid() gives that count) and writes one word per
+ * wavefront to sink_dev (uint32 [4 * grid]).
+ */
+qpn_status qpn_read_ceiling(const void* buf_dev, size_t bytes, uint32_t* sink_dev,
+                            int32_t grid, void* stream);
+int32_t qpn_read_ceiling_grid(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QPN_H */

@@ -1,0 +1,171 @@
+"""Python binding of libqpn.so, the weight-streaming skinny GEMM for MI355X.
+
+``quantized_weight_skinny_amd.qpn_*`` mirror the C entry points of
+``include/qpn.h`` one for one: integer device pointers and sizes in, the
+qpn_status code checked (a negative status raises ``QpnError``). Nothing here
+computes: every step runs in the HIP kernels of the library. The torch-facing
+helpers in ``quantized_weight_skinny_amd.torch_api`` only allocate device
+memory and pass pointers and the current stream.
+
+The library is loaded on first use; if it has not been built the call fails
+loudly (there is no fallback path).
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqpn.so")
+
+QPN_OK = 0
+QPN_ERR_INVALID_ARG = -1
+QPN_ERR_UNSUPPORTED = -2
+QPN_ERR_BAD_CODE = -3
+QPN_ERR_BUFFER_TOO_SMALL = -4
+QPN_ERR_HIP = -5
+
+QPN_FMT_NVFP4 = 1
+QPN_FMT_FP8_E4M3 = 2
+QPN_MAX_M = 16
+
+
+class QpnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {qpn_status_string(status)} ({status})")
+
+
+class qpn_weight(ctypes.Structure):
+    _fields_ = [
+        ("format", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("packed", ctypes.c_void_p),
+        ("tensor_scale", ctypes.c_float),
+        ("row_scales", ctypes.c_void_p),
+    ]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+_W = ctypes.POINTER(qpn_weight)
+
+# name -> (restype, argtypes); the declarations of include/qpn.h
+SIGNATURES = {
+    "qpn_status_string": (ctypes.c_char_p, [_I32]),
+    "qpn_packed_bytes": (_SZ, [_I32, _I64, _I64]),
+    "qpn_pack_nvfp4": (_I32, [_P, _P, _I64, _I64, _P, _SZ, _P, _P]),
+    "qpn_pack_fp8": (_I32, [_P, _I64, _I64, _P, _SZ, _P, _P]),
+    "qpn_unpack_nvfp4": (_I32, [_P, _SZ, _I64, _I64, _P, _P, _P]),
+    "qpn_unpack_fp8": (_I32, [_P, _SZ, _I64, _I64, _P, _P]),
+    "qpn_absmax_f32": (_I32, [_P, _I64, _P, _P]),
+    "qpn_nvfp4_tensor_scale": (_F, [_F]),
+    "qpn_quantize_nvfp4": (_I32, [_P, _I64, _I64, _F, _P, _P, _P]),
+    "qpn_quantize_fp8": (_I32, [_P, _I64, _I64, _P, _P, _P]),
+    "qpn_workspace_bytes": (_SZ, [_W, _I32]),
+    "qpn_workspace_bytes_split": (_SZ, [_W, _I32, _I32]),
+    "qpn_gemm": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
+    "qpn_gemm_tuned": (_I32, [_P, _W, _P, _I32, _P, _SZ, _I32, _I32, _P]),
+    "qpn_read_ceiling": (_I32, [_P, _SZ, _P, _I32, _P]),
+    "qpn_read_ceiling_grid": (_I32, []),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libqpn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m quantized_weight_skinny_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status, where):
+    if status != QPN_OK:
+        raise QpnError(status, where)
+    return status
+
+
+def qpn_status_string(status):
+    return lib().qpn_status_string(status).decode()
+
+
+def qpn_packed_bytes(fmt, n, k):
+    return lib().qpn_packed_bytes(fmt, n, k)
+
+
+def qpn_pack_nvfp4(codes, block_scales, n, k, packed, packed_bytes, bad_codes, stream):
+    return _check(lib().qpn_pack_nvfp4(codes, block_scales, n, k, packed, packed_bytes, bad_codes, stream),
+                  "qpn_pack_nvfp4")
+
+
+def qpn_pack_fp8(codes, n, k, packed, packed_bytes, bad_codes, stream):
+    return _check(lib().qpn_pack_fp8(codes, n, k, packed, packed_bytes, bad_codes, stream), "qpn_pack_fp8")
+
+
+def qpn_unpack_nvfp4(packed, packed_bytes, n, k, codes, block_scales, stream):
+    return _check(lib().qpn_unpack_nvfp4(packed, packed_bytes, n, k, codes, block_scales, stream),
+                  "qpn_unpack_nvfp4")
+
+
+def qpn_unpack_fp8(packed, packed_bytes, n, k, codes, stream):
+    return _check(lib().qpn_unpack_fp8(packed, packed_bytes, n, k, codes, stream), "qpn_unpack_fp8")
+
+
+def qpn_absmax_f32(x, count, out, stream):
+    return _check(lib().qpn_absmax_f32(x, count, out, stream), "qpn_absmax_f32")
+
+
+def qpn_nvfp4_tensor_scale(amax):
+    return lib().qpn_nvfp4_tensor_scale(amax)
+
+
+def qpn_quantize_nvfp4(w, n, k, tensor_scale, codes, block_scales, stream):
+    return _check(lib().qpn_quantize_nvfp4(w, n, k, tensor_scale, codes, block_scales, stream),
+                  "qpn_quantize_nvfp4")
+
+
+def qpn_quantize_fp8(w, n, k, codes, row_scales, stream):
+    return _check(lib().qpn_quantize_fp8(w, n, k, codes, row_scales, stream), "qpn_quantize_fp8")
+
+
+def make_weight(fmt, n, k, packed, tensor_scale=1.0, row_scales=None):
+    return qpn_weight(fmt, 0, n, k, packed, tensor_scale, row_scales)
+
+
+def qpn_workspace_bytes(weight, m):
+    return lib().qpn_workspace_bytes(ctypes.byref(weight), m)
+
+
+def qpn_workspace_bytes_split(weight, m, split_k):
+    return lib().qpn_workspace_bytes_split(ctypes.byref(weight), m, split_k)
+
+
+def qpn_gemm(x, weight, y, m, workspace, workspace_bytes, stream):
+    return _check(lib().qpn_gemm(x, ctypes.byref(weight), y, m, workspace, workspace_bytes, stream), "qpn_gemm")
+
+
+def qpn_gemm_tuned(x, weight, y, m, workspace, workspace_bytes, split_k, waves_per_group, stream):
+    return _check(lib().qpn_gemm_tuned(x, ctypes.byref(weight), y, m, workspace, workspace_bytes, split_k,
+                                       waves_per_group, stream), "qpn_gemm_tuned")
+
+
+def qpn_read_ceiling(buf, nbytes, sink, grid, stream):
+    return _check(lib().qpn_read_ceiling(buf, nbytes, sink, grid, stream), "qpn_read_ceiling")
+
+
+def qpn_read_ceiling_grid():
+    return lib().qpn_read_ceiling_grid()

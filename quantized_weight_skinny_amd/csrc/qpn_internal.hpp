@@ -1,0 +1,47 @@
+// Host-side declarations shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qpn {
+
+// Launch plan of one GEMM call: the K range is cut into `split` pieces of
+// `units_per_split` 256-element units; each workgroup of `waves` wavefronts
+// handles `waves` n-tiles of one piece. split > 1 writes fp32 partial sums to
+// the workspace and a second kernel adds them in piece order.
+struct GemmPlan {
+  int split;
+  int waves;
+  int units_per_split;
+  int lds_stride;  // halves per staged activation row
+  size_t lds_bytes;
+  size_t workspace_bytes;
+};
+
+bool plan_gemm(int fmt, int64_t n, int64_t k, int m, int split_override, int waves_override,
+               GemmPlan* plan);
+
+hipError_t launch_gemm(int fmt, const GemmPlan& plan, const void* x, const void* packed,
+                       const float* row_scales, float tensor_scale, void* y, void* workspace,
+                       int m, int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                             void* packed, int32_t* bad, hipStream_t stream);
+hipError_t launch_pack_fp8(const uint8_t* codes, int64_t n, int64_t k, void* packed,
+                           int32_t* bad, hipStream_t stream);
+hipError_t launch_unpack_nvfp4(const void* packed, int64_t n, int64_t k, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream);
+hipError_t launch_unpack_fp8(const void* packed, int64_t n, int64_t k, uint8_t* codes,
+                             hipStream_t stream);
+hipError_t launch_absmax(const float* x, int64_t count, float* out, hipStream_t stream);
+hipError_t launch_quantize_nvfp4(const float* w, int64_t n, int64_t k, float tensor_scale,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_quantize_fp8(const float* w, int64_t n, int64_t k, uint8_t* codes,
+                               float* row_scales, hipStream_t stream);
+hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, int grid,
+                               hipStream_t stream);
+int read_ceiling_default_grid();
+
+}  // namespace qpn

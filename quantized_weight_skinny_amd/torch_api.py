@@ -1,0 +1,181 @@
+"""torch plumbing around the libqpn entry points.
+
+torch supplies device memory and the current HIP stream; each helper passes
+pointers to one C entry point of the library (see ``include/qpn.h``) and
+returns the tensors it allocated. No arithmetic of the method happens here.
+"""
+
+import torch
+
+from . import (
+    QPN_ERR_BAD_CODE,
+    QPN_FMT_FP8_E4M3,
+    QPN_FMT_NVFP4,
+    QpnError,
+    make_weight,
+    qpn_absmax_f32,
+    qpn_gemm,
+    qpn_gemm_tuned,
+    qpn_nvfp4_tensor_scale,
+    qpn_pack_fp8,
+    qpn_pack_nvfp4,
+    qpn_packed_bytes,
+    qpn_quantize_fp8,
+    qpn_quantize_nvfp4,
+    qpn_read_ceiling,
+    qpn_read_ceiling_grid,
+    qpn_unpack_fp8,
+    qpn_unpack_nvfp4,
+    qpn_workspace_bytes,
+    qpn_workspace_bytes_split,
+)
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _cuda(t, dtype, name):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    return t
+
+
+class PackedWeight:
+    """A packed [n, k] weight on the device plus its scales."""
+
+    def __init__(self, fmt, n, k, packed, tensor_scale=1.0, row_scales=None):
+        self.fmt, self.n, self.k = fmt, n, k
+        self.packed = packed
+        self.tensor_scale = float(tensor_scale)
+        self.row_scales = row_scales
+
+    def desc(self):
+        rs = self.row_scales.data_ptr() if self.row_scales is not None else None
+        return make_weight(self.fmt, self.n, self.k, self.packed.data_ptr(), self.tensor_scale, rs)
+
+    @property
+    def nbytes(self):
+        """Bytes the GEMM streams for this weight (packed codes and scales,
+        plus the fp32 row scales of FP8)."""
+        extra = self.row_scales.numel() * 4 if self.row_scales is not None else 0
+        return self.packed.numel() + extra
+
+
+def _raise_bad(bad, where):
+    count = int(bad.item())
+    if count:
+        raise QpnError(QPN_ERR_BAD_CODE, f"{where}: {count} NaN E4M3 code(s)")
+
+
+def pack_nvfp4(codes, block_scales, tensor_scale, n, k, check=True):
+    """Canonical NVFP4 codes [n, k/2] + E4M3 block scales [n, k/16] -> PackedWeight."""
+    _cuda(codes, torch.uint8, "codes")
+    _cuda(block_scales, torch.uint8, "block_scales")
+    nbytes = qpn_packed_bytes(QPN_FMT_NVFP4, n, k)
+    packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=codes.device) if check else None
+    qpn_pack_nvfp4(codes.data_ptr(), block_scales.data_ptr(), n, k, packed.data_ptr(), nbytes,
+                   bad.data_ptr() if check else None, _stream())
+    if check:
+        _raise_bad(bad, "qpn_pack_nvfp4")
+    return PackedWeight(QPN_FMT_NVFP4, n, k, packed[:nbytes] if nbytes else packed, tensor_scale)
+
+
+def pack_fp8(codes, row_scales, n, k, check=True):
+    """Canonical E4M3 codes [n, k] + fp32 row scales [n] -> PackedWeight."""
+    _cuda(codes, torch.uint8, "codes")
+    _cuda(row_scales, torch.float32, "row_scales")
+    nbytes = qpn_packed_bytes(QPN_FMT_FP8_E4M3, n, k)
+    packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=codes.device) if check else None
+    qpn_pack_fp8(codes.data_ptr(), n, k, packed.data_ptr(), nbytes, bad.data_ptr() if check else None,
+                 _stream())
+    if check:
+        _raise_bad(bad, "qpn_pack_fp8")
+    return PackedWeight(QPN_FMT_FP8_E4M3, n, k, packed[:nbytes] if nbytes else packed, 1.0, row_scales)
+
+
+def unpack(pw):
+    """PackedWeight -> canonical tensors (codes, block scales) or (codes,)."""
+    dev = pw.packed.device
+    if pw.fmt == QPN_FMT_NVFP4:
+        codes = torch.empty((pw.n, pw.k // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((pw.n, pw.k // 16), dtype=torch.uint8, device=dev)
+        qpn_unpack_nvfp4(pw.packed.data_ptr(), pw.packed.numel(), pw.n, pw.k, codes.data_ptr(),
+                         scales.data_ptr(), _stream())
+        return codes, scales
+    codes = torch.empty((pw.n, pw.k), dtype=torch.uint8, device=dev)
+    qpn_unpack_fp8(pw.packed.data_ptr(), pw.packed.numel(), pw.n, pw.k, codes.data_ptr(), _stream())
+    return (codes,)
+
+
+def absmax(w):
+    """max |w| over a float32 CUDA tensor, computed by the library (returns a
+    1-element device tensor)."""
+    _cuda(w, torch.float32, "w")
+    out = torch.empty(1, dtype=torch.float32, device=w.device)
+    qpn_absmax_f32(w.data_ptr(), w.numel(), out.data_ptr(), _stream())
+    return out
+
+
+def nvfp4_tensor_scale(amax):
+    return qpn_nvfp4_tensor_scale(float(amax))
+
+
+def quantize_nvfp4(w, tensor_scale=None):
+    """float32 W [n, k] on the device -> (codes [n, k/2], block scales [n, k/16], s_t)."""
+    _cuda(w, torch.float32, "w")
+    n, k = w.shape
+    if tensor_scale is None:
+        amax = absmax(w).item()
+        if amax != amax or amax == float("inf"):
+            raise ValueError("weights must be finite")
+        tensor_scale = nvfp4_tensor_scale(amax)
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // 16), dtype=torch.uint8, device=w.device)
+    qpn_quantize_nvfp4(w.data_ptr(), n, k, tensor_scale, codes.data_ptr(), scales.data_ptr(), _stream())
+    return codes, scales, tensor_scale
+
+
+def quantize_fp8(w):
+    """float32 W [n, k] on the device -> (codes [n, k], row scales [n])."""
+    _cuda(w, torch.float32, "w")
+    n, k = w.shape
+    codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    rs = torch.empty(n, dtype=torch.float32, device=w.device)
+    qpn_quantize_fp8(w.data_ptr(), n, k, codes.data_ptr(), rs.data_ptr(), _stream())
+    return codes, rs
+
+
+def workspace_bytes(pw, m, split_k=0):
+    d = pw.desc()
+    return qpn_workspace_bytes_split(d, m, split_k) if split_k else qpn_workspace_bytes(d, m)
+
+
+def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0):
+    """y[m, n] = x[m, k] @ dequant(W)^T in fp16 through qpn_gemm."""
+    _cuda(x, torch.float16, "x")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
+    d = pw.desc()
+    need = qpn_workspace_bytes_split(d, m, split_k) if split_k else qpn_workspace_bytes(d, m)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if need else 0
+    if split_k or waves:
+        qpn_gemm_tuned(x.data_ptr(), d, out.data_ptr(), m, ws_ptr, ws_bytes, split_k, waves, _stream())
+    else:
+        qpn_gemm(x.data_ptr(), d, out.data_ptr(), m, ws_ptr, ws_bytes, _stream())
+    return out
+
+
+def read_ceiling(buf, grid=0, sink=None):
+    """One pass of the read-only streaming kernel over a uint8 CUDA tensor."""
+    g = grid or qpn_read_ceiling_grid()
+    if sink is None:
+        sink = torch.empty(g * 4, dtype=torch.int32, device=buf.device)
+    qpn_read_ceiling(buf.data_ptr(), buf.numel() - buf.numel() % 16, sink.data_ptr(), g, _stream())
+    return sink

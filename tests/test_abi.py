@@ -1,0 +1,134 @@
+"""CPU checks of libqpn.so: it loads, exports every entry point of
+include/qpn.h, and rejects bad arguments on the host before any HIP call
+(so these run without a GPU; no compute entry point is exercised)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_weight_skinny_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qpn.h")
+
+FAKE = 0x7F0000000000  # an aligned non-null "device" address; never dereferenced
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qpn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = q.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 15
+    for name in declared:
+        assert hasattr(lib, name), name
+        assert name in q.SIGNATURES, name
+    assert set(q.SIGNATURES) == set(declared)
+
+
+def test_status_strings():
+    assert q.qpn_status_string(q.QPN_OK) == "ok"
+    assert q.qpn_status_string(q.QPN_ERR_BUFFER_TOO_SMALL) == "buffer too small"
+    assert q.qpn_status_string(-99) == "unknown status"
+
+
+def test_packed_bytes():
+    assert q.qpn_packed_bytes(q.QPN_FMT_NVFP4, 512, 1024) == 32 * 4 * 2304
+    assert q.qpn_packed_bytes(q.QPN_FMT_FP8_E4M3, 512, 1024) == 32 * 4 * 4096
+    # ragged shapes round up to whole 16 x 256 tiles
+    assert q.qpn_packed_bytes(q.QPN_FMT_NVFP4, 17, 48) == 2 * 1 * 2304
+    assert q.qpn_packed_bytes(q.QPN_FMT_NVFP4, 34816, 5120) == 2176 * 20 * 2304
+    # the 27B gate_up matrix: codes + scales exactly, no padding
+    assert q.qpn_packed_bytes(q.QPN_FMT_NVFP4, 34816, 5120) == 34816 * 5120 // 2 + 34816 * 5120 // 16
+    assert q.qpn_packed_bytes(q.QPN_FMT_NVFP4, 0, 1024) == 0
+    assert q.qpn_packed_bytes(q.QPN_FMT_NVFP4, 16, 24) == 0       # K % 16
+    assert q.qpn_packed_bytes(3, 16, 32) == 0                      # unknown format
+    assert q.qpn_packed_bytes(q.QPN_FMT_FP8_E4M3, -1, 32) == 0
+
+
+def test_tensor_scale_helper():
+    assert q.qpn_nvfp4_tensor_scale(2688.0) == 1.0
+    assert q.qpn_nvfp4_tensor_scale(0.0) == 1.0
+
+
+def _w(fmt=q.QPN_FMT_NVFP4, n=512, k=1024, packed=FAKE, rs=FAKE):
+    return q.make_weight(fmt, n, k, packed, 1.0, rs)
+
+
+def _gemm(x, w, y, m, ws=None, wsb=0, split=0, waves=0):
+    return q.lib().qpn_gemm_tuned(x, ctypes.byref(w), y, m, ws, wsb, split, waves, None)
+
+
+def test_gemm_rejects_bad_arguments_before_any_device_call():
+    err = q.QPN_ERR_INVALID_ARG
+    assert _gemm(FAKE, _w(), FAKE, 17) == err                 # m > 16
+    assert _gemm(FAKE, _w(), FAKE, -1) == err
+    assert _gemm(None, _w(), FAKE, 1) == err                  # null x
+    assert _gemm(FAKE + 8, _w(), FAKE, 1) == err              # x not 16-byte aligned
+    assert _gemm(FAKE, _w(), None, 1) == err                  # null y
+    assert _gemm(FAKE, _w(packed=None), FAKE, 1) == err       # null packed
+    assert _gemm(FAKE, _w(packed=FAKE + 4), FAKE, 1) == err   # misaligned packed
+    assert _gemm(FAKE, _w(k=1000), FAKE, 1) == err            # k % 16
+    assert _gemm(FAKE, _w(fmt=9), FAKE, 1) == err             # format
+    assert _gemm(FAKE, _w(fmt=q.QPN_FMT_FP8_E4M3, rs=None), FAKE, 1) == err  # FP8 needs row scales
+    assert _gemm(FAKE, _w(), FAKE, 1, waves=5) == err
+    w = _w()
+    w.reserved = 1
+    assert _gemm(FAKE, w, FAKE, 1) == err
+    bad_scale = q.make_weight(q.QPN_FMT_NVFP4, 512, 1024, FAKE, float("nan"), None)
+    assert _gemm(FAKE, bad_scale, FAKE, 1) == err
+
+
+def test_gemm_empty_problems_are_noops():
+    assert _gemm(None, _w(), None, 0) == q.QPN_OK            # m == 0
+    assert _gemm(None, _w(n=0), None, 4) == q.QPN_OK         # n == 0
+
+
+def test_gemm_workspace_checks():
+    w = _w(n=5120, k=17408)
+    need = q.qpn_workspace_bytes(w, 8)
+    assert need > 0                                           # small N splits K
+    assert _gemm(FAKE, w, FAKE, 8, None, 0) == q.QPN_ERR_INVALID_ARG
+    assert _gemm(FAKE, w, FAKE, 8, FAKE, need - 16) == q.QPN_ERR_BUFFER_TOO_SMALL
+    assert q.qpn_workspace_bytes_split(w, 8, 5) == 5 * 8 * 5120 * 4
+    # one K range of 17408 x 8 rows does not fit the activation stage in LDS
+    assert q.qpn_workspace_bytes_split(w, 8, 1) == 0
+    assert _gemm(FAKE, w, FAKE, 8, FAKE, need, split=1) == q.QPN_ERR_UNSUPPORTED
+    assert q.qpn_workspace_bytes_split(_w(n=5120, k=4096), 1, 1) == 0
+    # gate_up at M=1 fills the chip without splitting K
+    assert q.qpn_workspace_bytes(_w(n=34816, k=5120), 1) == 0
+    assert q.qpn_workspace_bytes(_w(), 17) == 0
+
+
+def test_pack_and_quantize_reject_bad_arguments():
+    lib = q.lib()
+    nv = q.qpn_packed_bytes(q.QPN_FMT_NVFP4, 32, 64)
+    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 64, FAKE, nv - 1, None, None) == q.QPN_ERR_BUFFER_TOO_SMALL
+    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 64, FAKE + 8, nv, None, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_pack_nvfp4(None, FAKE, 32, 64, FAKE, nv, None, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 40, FAKE, nv, None, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_pack_nvfp4(None, None, 0, 64, None, 0, None, None) == q.QPN_OK  # empty
+    f8 = q.qpn_packed_bytes(q.QPN_FMT_FP8_E4M3, 32, 64)
+    assert lib.qpn_pack_fp8(FAKE, 32, 64, FAKE, f8 - 16, None, None) == q.QPN_ERR_BUFFER_TOO_SMALL
+    assert lib.qpn_unpack_fp8(FAKE, f8, -2, 64, FAKE, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_quantize_nvfp4(FAKE, 4, 64, 0.0, FAKE, FAKE, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_quantize_nvfp4(FAKE, 4, 64, float("inf"), FAKE, FAKE, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_quantize_fp8(FAKE, 4, 64, FAKE, None, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_absmax_f32(FAKE, -1, FAKE, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_read_ceiling(FAKE, 100, FAKE, 0, None) == q.QPN_ERR_INVALID_ARG  # bytes % 16
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "quantized_weight_skinny_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f

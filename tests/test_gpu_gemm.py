@@ -1,0 +1,192 @@
+"""GPU parity of qpn_gemm (through the C ABI) against the float64 oracle.
+
+Bar: |y_gpu - y_ref| <= 2e-3 * sum_k |x * w| + 1e-3 per element; exact where
+the arithmetic is exact (one-hot activations, negation, repeat runs)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import (DEV, assert_within_tolerance, gpu_quantize, oracle_quantize, oracle_y,
+                         say, to_dev, to_host)
+from quantized_weight_skinny_amd import torch_api as qt
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [(512, 1024), (37, 48), (100, 272), (16, 4096), (33, 2304), (300, 5120)]
+
+
+def _parity(fmt, m, n, k, seed, **kw):
+    w = workloads.weights(n, k, seed)
+    x = workloads.activations(m, k, seed + 1)
+    pw, _ = gpu_quantize(fmt, to_dev(w))
+    y = to_host(qt.gemm(to_dev(x), pw, **kw))
+    parts = oracle_quantize(fmt, w)
+    y_ref, b = oracle_y(fmt, x, parts)
+    assert_within_tolerance(y, y_ref, b, f"{fmt} m={m} n={n} k={k} {kw}")
+    return y
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("n,k", SMALL)
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 16])
+def test_gemm_parity_small(fmt, m, n, k):
+    say("gemm", fmt, m, n, k)
+    _parity(fmt, m, n, k, seed=1000 + n + k + m)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("split,waves", [(1, 4), (2, 4), (3, 8), (5, 4), (7, 8), (0, 8)])
+def test_gemm_launch_shapes_agree(fmt, split, waves):
+    n, k, m = 96, 1792, 5
+    say("gemm tuned", fmt, split, waves)
+    _parity(fmt, m, n, k, seed=77, split_k=split, waves=waves)
+
+
+def test_gemm_vs_hand_case():
+    say("gemm hand case")
+    from golden_io import load_case
+    case = load_case("nvfp4_hand_case.json")
+    codes, scales, s_t = qt.quantize_nvfp4(to_dev(case["W"]))
+    pw = qt.pack_nvfp4(codes, scales, s_t, 2, 32)
+    y = to_host(qt.gemm(to_dev(case["x"]), pw))
+    # every partial sum of the hand case is exact in fp32, so the only rounding
+    # is the final one to fp16 (nearest even)
+    assert np.array_equal(y, case["y"].astype(np.float16))
+
+
+def _one_hot_check(fmt, n, k, s_t=1.0):
+    if fmt == "nvfp4":
+        codes = workloads.random_nibble_bytes(n, k, 5)
+        scales = workloads.random_block_scale_codes(n, k, 6)
+        pw = qt.pack_nvfp4(to_dev(codes), to_dev(scales), s_t, n, k)
+        wdq = oracle.dequantize_nvfp4(oracle.unpack_nibbles(codes), scales, s_t)
+    else:
+        codes = workloads.random_fp8_codes(n, k, 7)
+        rs = np.full(n, s_t, np.float32)
+        pw = qt.pack_fp8(to_dev(codes), to_dev(rs), n, k)
+        wdq = oracle.dequantize_fp8(codes, rs)
+    ks = [0, 1, 7, 8, 15, 16, 31, 63, 64, 255, k - 1]
+    x = np.zeros((len(ks), k), np.float16)
+    for i, kk in enumerate(ks):
+        x[i, kk] = 1.0
+    y = to_host(qt.gemm(to_dev(x), pw))
+    for i, kk in enumerate(ks):
+        want = wdq[:, kk]
+        assert np.all(np.abs(want) < 65504)
+        assert np.array_equal(y[i].astype(np.float64), want), (fmt, kk)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_one_hot_reads_back_every_weight_exactly(fmt):
+    """x = e_k picks one weight column: decoding must be bit-exact."""
+    say("one hot", fmt)
+    _one_hot_check(fmt, 64, 512)
+    _one_hot_check(fmt, 20, 272, s_t=0.25)
+
+
+def test_fp8_one_hot_covers_all_codes():
+    say("fp8 all codes")
+    n, k = 16, 256
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F] * 17, np.uint8)[: n * k].reshape(n, k)
+    rs = np.ones(n, np.float32)
+    pw = qt.pack_fp8(to_dev(codes), to_dev(rs), n, k)
+    wdq = oracle.dequantize_fp8(codes, rs)
+    x = np.eye(k, dtype=np.float16)[:16]
+    for start in range(0, k, 16):
+        x = np.eye(k, dtype=np.float16)[start:start + 16]
+        y = to_host(qt.gemm(to_dev(x), pw))
+        assert np.array_equal(y.astype(np.float64), wdq[:, start:start + 16].T)
+
+
+def test_negation_and_repeat_are_bit_exact():
+    say("negation / determinism")
+    n, k, m = 300, 5120, 8
+    w = workloads.weights(n, k, 9)
+    x = workloads.activations(m, k, 10)
+    for fmt in ("nvfp4", "fp8"):
+        pw, _ = gpu_quantize(fmt, to_dev(w))
+        xd = to_dev(x)
+        y1 = to_host(qt.gemm(xd, pw))
+        y2 = to_host(qt.gemm(xd, pw))
+        yn = to_host(qt.gemm(-xd, pw))
+        assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+        assert np.array_equal(yn, -y1)
+
+
+def test_rows_of_a_batch_match_single_row_calls():
+    say("batch rows")
+    n, k = 128, 1024
+    w = workloads.weights(n, k, 12)
+    x = workloads.activations(8, k, 13)
+    pw, _ = gpu_quantize("nvfp4", to_dev(w))
+    y8 = to_host(qt.gemm(to_dev(x), pw))
+    for r in range(8):
+        y1 = to_host(qt.gemm(to_dev(x[r:r + 1]), pw))
+        # same per-column arithmetic for any M when K is not split differently
+        assert np.array_equal(y8[r], y1[0])
+
+
+def test_output_guard_bytes_untouched():
+    say("guard bytes")
+    n, k, m = 50, 512, 3
+    w = workloads.weights(n, k, 14)
+    pw, _ = gpu_quantize("nvfp4", to_dev(w))
+    buf = torch.full((m * n + 64,), 12345.0, dtype=torch.float16, device=DEV)
+    out = buf[:m * n].view(m, n)
+    qt.gemm(to_dev(workloads.activations(m, k, 15)), pw, out=out)
+    tail = to_host(buf[m * n:])
+    assert np.all(tail == np.float16(12345.0))
+
+
+def test_empty_and_degenerate_shapes():
+    say("degenerate shapes")
+    # K = 0: the empty sum
+    pw = qt.pack_nvfp4(torch.zeros((4, 0), dtype=torch.uint8, device=DEV),
+                       torch.zeros((4, 0), dtype=torch.uint8, device=DEV), 1.0, 4, 0)
+    x = torch.zeros((2, 0), dtype=torch.float16, device=DEV)
+    y = torch.full((2, 4), 7.0, dtype=torch.float16, device=DEV)
+    qt.gemm(x, pw, out=y)
+    assert not to_host(y).any()
+    # M = 0 and N = 0 do nothing
+    pw2, _ = gpu_quantize("nvfp4", to_dev(workloads.weights(16, 32, 1)))
+    qt.gemm(torch.zeros((0, 32), dtype=torch.float16, device=DEV), pw2)
+    # N = 1, K = 16: a single block
+    _parity("nvfp4", 1, 1, 16, seed=3)
+    _parity("fp8", 3, 1, 16, seed=4)
+
+
+FULL = [
+    ("nvfp4", "gate_up", 1), ("nvfp4", "down", 1),
+    ("nvfp4", "gate_up", 8), ("nvfp4", "down", 8), ("nvfp4", "qkv", 8), ("nvfp4", "o_proj", 8),
+    ("fp8", "qkv", 1), ("fp8", "qkv", 4), ("fp8", "down", 2), ("fp8", "down", 4),
+    ("nvfp4", "lm_head", 8),
+]
+
+
+@pytest.mark.parametrize("fmt,matrix,m", FULL)
+def test_full_size_sampled_outputs(fmt, matrix, m):
+    """27B-shaped matrices in the launch configuration the bench times; the
+    oracle recomputes a sample of output columns (every row of x)."""
+    n, k = workloads.SHAPES[matrix]
+    say("full size", fmt, matrix, m, n, k)
+    wl = "nvfp4_27b_m8" if fmt == "nvfp4" else "fp8_27b_m124"
+    w = workloads.weights(n, k, workloads.seed_for(wl, matrix, "W"))
+    x = workloads.activations(m, k, workloads.seed_for(wl, matrix, "x"))
+    wd = to_dev(w)
+    pw, _ = gpu_quantize(fmt, wd)
+    del wd
+    y = to_host(qt.gemm(to_dev(x), pw))
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n),
+                                     np.random.default_rng(n + m).integers(0, n, 96)]))
+    if fmt == "nvfp4":
+        parts = oracle.quantize_nvfp4(w[cols], tensor_scale=oracle.nvfp4_tensor_scale(np.abs(w).max()))
+    else:
+        parts = oracle.quantize_fp8(w[cols])
+    y_ref, b = oracle_y(fmt, x, parts)
+    assert_within_tolerance(y[:, cols], y_ref, b, f"{fmt} {matrix} m={m}")
+    assert np.isfinite(y).all()
+    del pw
+    torch.cuda.empty_cache()

@@ -1,0 +1,163 @@
+"""GPU parity of the offline kernels: absmax, the NVFP4/FP8 quantizers and
+pack/unpack, all bit-exact against the oracle (integer and byte work)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from golden_io import load_case
+from gpu_helpers import DEV, oracle_quantize, say, to_dev, to_host
+from quantized_weight_skinny_amd import QPN_ERR_BAD_CODE, QpnError
+from quantized_weight_skinny_amd import torch_api as qt
+
+pytestmark = pytest.mark.gpu
+
+
+def test_absmax_exact_and_nan():
+    say("absmax")
+    for n in (0, 1, 255, 4097, 1 << 20):
+        v = workloads.weights(1, n, 5 + n)[0] if n else np.zeros(0, np.float32)
+        got = to_host(qt.absmax(to_dev(v)))[0]
+        assert got == (np.abs(v).max() if n else 0.0)
+    v = np.ones(1000, np.float32)
+    v[777] = np.nan
+    assert np.isnan(to_host(qt.absmax(to_dev(v)))[0])
+
+
+def test_quantize_nvfp4_hand_case():
+    say("quantize nvfp4 hand case")
+    case = load_case("nvfp4_hand_case.json")
+    codes, scales, s_t = qt.quantize_nvfp4(to_dev(case["W"]))
+    assert s_t == case["tensor_scale"]
+    assert np.array_equal(to_host(codes), case["packed_codes"])
+    assert np.array_equal(to_host(scales), case["block_scale_codes"])
+
+
+def test_quantize_fp8_hand_case():
+    say("quantize fp8 hand case")
+    case = load_case("fp8_hand_case.json")
+    codes, rs = qt.quantize_fp8(to_dev(case["W"]))
+    assert np.array_equal(to_host(codes), case["codes"])
+    assert np.array_equal(to_host(rs), case["row_scales"])
+
+
+SHAPES = [(512, 1024), (37, 48), (16, 272), (100, 2320), (1, 16)]
+
+
+def _edge_weights(n, k, seed):
+    """Random weights with ties, zeros, signed zeros, subnormals and spikes."""
+    rng = np.random.default_rng(seed)
+    w = workloads.weights(n, k, seed)
+    mask = rng.random((n, k))
+    w[mask < 0.05] = 0.0
+    w[(mask >= 0.05) & (mask < 0.08)] = -0.0
+    w[(mask >= 0.08) & (mask < 0.10)] *= 1e-36          # fp32 subnormals
+    w[(mask >= 0.10) & (mask < 0.12)] = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], 1)[0]
+    w[(mask >= 0.99)] *= 50.0
+    w[0, :16] = 0.0                                        # an all-zero block
+    return w.astype(np.float32)
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("edge", [False, True])
+def test_quantize_nvfp4_matches_oracle(n, k, edge):
+    say("quantize nvfp4", n, k, edge)
+    w = _edge_weights(n, k, 31 + n) if edge else workloads.weights(n, k, 31 + n)
+    codes, scales, s_t = qt.quantize_nvfp4(to_dev(w))
+    rc, rsc, rst = oracle_quantize("nvfp4", w)
+    assert np.float32(s_t) == rst
+    assert np.array_equal(to_host(scales), rsc)
+    assert np.array_equal(to_host(codes), oracle.pack_nibbles(rc))
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("edge", [False, True])
+def test_quantize_fp8_matches_oracle(n, k, edge):
+    say("quantize fp8", n, k, edge)
+    w = _edge_weights(n, k, 41 + n) if edge else workloads.weights(n, k, 41 + n)
+    codes, rs = qt.quantize_fp8(to_dev(w))
+    rc, rrs = oracle_quantize("fp8", w)
+    assert np.array_equal(to_host(rs), rrs)
+    assert np.array_equal(to_host(codes), rc)
+
+
+@pytest.mark.parametrize("matrix", ["gate_up", "down", "lm_head"])
+def test_quantize_full_size_sampled_rows(matrix):
+    """Whole 27B-shaped matrices quantized on the GPU; the oracle redoes a
+    sample of rows (with its own tensor scale, which must agree)."""
+    n, k = workloads.SHAPES[matrix]
+    say("quantize full size", matrix, n, k)
+    w = workloads.weights(n, k, workloads.seed_for("nvfp4_27b_m1", matrix, "W"))
+    wd = to_dev(w)
+    codes, scales, s_t = qt.quantize_nvfp4(wd)
+    amax = np.abs(w).max()
+    rows = np.unique(np.concatenate([[0, 1, n - 1], np.random.default_rng(1).integers(0, n, 40)]))
+    rc, rsc, rst = oracle.quantize_nvfp4(w[rows], tensor_scale=oracle.nvfp4_tensor_scale(amax))
+    assert np.float32(s_t) == rst
+    sel = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(to_host(scales.index_select(0, sel)), rsc)
+    assert np.array_equal(to_host(codes.index_select(0, sel)), oracle.pack_nibbles(rc))
+    if matrix != "lm_head":
+        c8, r8 = qt.quantize_fp8(wd)
+        oc, ors = oracle.quantize_fp8(w[rows])
+        assert np.array_equal(to_host(r8.index_select(0, sel)), ors)
+        assert np.array_equal(to_host(c8.index_select(0, sel)), oc)
+    del wd
+    torch.cuda.empty_cache()
+
+
+PACK_SHAPES = [(512, 1024), (17, 48), (33, 272), (16, 256), (1, 16), (130, 4112)]
+
+
+@pytest.mark.parametrize("n,k", PACK_SHAPES)
+def test_pack_unpack_nvfp4_round_trip(n, k):
+    say("pack nvfp4", n, k)
+    codes = workloads.random_nibble_bytes(n, k, n * 7 + k)
+    scales = workloads.random_block_scale_codes(n, k, n * 11 + k, lo=0, hi=0xFE)
+    scales = np.where((scales & 0x7F) == 0x7F, scales ^ 1, scales).astype(np.uint8)
+    pw = qt.pack_nvfp4(to_dev(codes), to_dev(scales), 1.0, n, k)
+    c2, s2 = qt.unpack(pw)
+    assert np.array_equal(to_host(c2), codes)
+    assert np.array_equal(to_host(s2), scales)
+    # every padding byte (rows past n, columns past k) is zero
+    raw = to_host(pw.packed)
+    nt, ku = -(-n // 16), -(-k // 256)
+    units = raw.reshape(nt, ku, 2304)
+    lane = np.arange(64)
+    r, g = lane % 16, lane // 16
+    for t in range(nt):
+        for u in range(ku):
+            for h in range(2):
+                vec = units[t, u, h * 1024:(h + 1) * 1024].reshape(64, 16)
+                row = t * 16 + r
+                k0 = u * 256 + g * 64 + h * 32
+                dead = (row >= n) | (k0 >= k)
+                assert not vec[dead].any()
+
+
+@pytest.mark.parametrize("n,k", PACK_SHAPES)
+def test_pack_unpack_fp8_round_trip(n, k):
+    say("pack fp8", n, k)
+    codes = workloads.random_fp8_codes(n, k, n * 13 + k)
+    rs = np.ones(n, np.float32)
+    pw = qt.pack_fp8(to_dev(codes), to_dev(rs), n, k)
+    (c2,) = qt.unpack(pw)
+    assert np.array_equal(to_host(c2), codes)
+
+
+def test_pack_counts_nan_codes():
+    say("pack nan codes")
+    n, k = 32, 512
+    codes = workloads.random_nibble_bytes(n, k, 3)
+    scales = workloads.random_block_scale_codes(n, k, 4)
+    scales[3, 5] = 0x7F
+    scales[30, 31] = 0xFF
+    with pytest.raises(QpnError) as e:
+        qt.pack_nvfp4(to_dev(codes), to_dev(scales), 1.0, n, k)
+    assert e.value.status == QPN_ERR_BAD_CODE and "2 NaN" in str(e.value)
+    f8 = workloads.random_fp8_codes(n, k, 5)
+    f8[0, 0] = 0x7F
+    with pytest.raises(QpnError):
+        qt.pack_fp8(to_dev(f8), to_dev(np.ones(n, np.float32)), n, k)
