@@ -82,39 +82,55 @@ class Mat:
         return self.weight_bytes + 2 * m * self.k + 2 * m * self.n
 
 
-def time_matrix(mat, m, iters, warm=5):
-    """Average µs per launch of one matrix, back to back over rotating copies,
-    timed with events on the launch stream."""
+def capture(launches):
+    """One HIP graph (torch.cuda.CUDAGraph) holding the given launch closures
+    in order; outputs and workspaces are allocated before capture and the
+    captured launches contain no memset."""
+    import torch
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in launches:
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_matrix(mat, m, reps=3):
+    """Average µs per launch of one matrix: a graph of back-to-back launches
+    over all rotating copies, timed with events on the launch stream."""
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
     x = torch.randn((m, mat.k), device="cuda").half()
     y = torch.empty((m, mat.n), dtype=torch.float16, device="cuda")
-    ws_need = max(qt.workspace_bytes(c, m) for c in mat.copies[:1])
-    ws = torch.empty(max(ws_need, 16), dtype=torch.uint8, device="cuda")
-    r = len(mat.copies)
-    for i in range(warm):
-        qt.gemm(x, mat.copies[i % r], out=y, workspace=ws)
+    ws = qt.new_workspace(mat.copies[0], m)
+    launches = [(lambda c=c: qt.gemm(x, c, out=y, workspace=ws)) for c in mat.copies]
+    for fn in launches:
+        fn()
+    g = capture(launches)
+    g.replay()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
-    for i in range(iters):
-        qt.gemm(x, mat.copies[i % r], out=y, workspace=ws)
+    for _ in range(reps):
+        g.replay()
     e1.record(s)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / iters
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(launches))
+    del g
     return us, mat.bytes_for(m) / (us * 1e-6) / 1e9
 
 
-def read_ceiling(nbytes=4 << 30, reps=8):
-    """Best read-only streaming bandwidth over a few grid sizes (GB/s)."""
+def read_ceiling(nbytes=4 << 30, reps=6):
+    """Best read-only streaming bandwidth over a sweep of grid sizes (GB/s)."""
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
     from quantized_weight_skinny_amd import qpn_read_ceiling_grid
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    base = qpn_read_ceiling_grid()
+    cus = qpn_read_ceiling_grid() // 8
     best = (0.0, 0)
-    for grid in (base // 4, base // 2, base, base * 2):
+    for grid in (cus, cus * 2, cus * 3, cus * 4, cus * 6, cus * 8):
         sink = torch.empty(grid * 4, dtype=torch.int32, device="cuda")
         qt.read_ceiling(buf, grid, sink)
         torch.cuda.synchronize()
@@ -194,57 +210,76 @@ def main():
     x2 = torch.randn((m, 17408), device="cuda").half()
     h = torch.empty((m, 34816), dtype=torch.float16, device="cuda")
     y = torch.empty((m, 5120), dtype=torch.float16, device="cuda")
-    ws = torch.empty(max(qt.workspace_bytes(down.copies[0], m), 16), dtype=torch.uint8, device="cuda")
+    ws_g = qt.new_workspace(gate_up.copies[0], m)
+    ws_d = qt.new_workspace(down.copies[0], m)
     step_bytes = gate_up.bytes_for(m) + down.bytes_for(m)
 
     def step(i):
-        qt.gemm(x1, gate_up.copies[i % r_steps], out=h)
-        qt.gemm(x2, down.copies[i % r_steps], out=y, workspace=ws)
+        qt.gemm(x1, gate_up.copies[i % r_steps], out=h, workspace=ws_g)
+        qt.gemm(x2, down.copies[i % r_steps], out=y, workspace=ws_d)
 
-    for i in range(args.warmup):
+    # One graph per rotating copy, each holding one step (gate_up then down):
+    # the timed loop replays exactly `steps` graphs, so no Python launch
+    # overhead sits between the kernels.
+    for i in range(r_steps):
         step(i)
     torch.cuda.synchronize()
+    eager_y = y.clone()
+    graphs = [capture([lambda i=i: step(i)]) for i in range(r_steps)]
+    for i in range(args.warmup):
+        graphs[i % r_steps].replay()
+    torch.cuda.synchronize()
+    graphs[(r_steps - 1)].replay()
+    torch.cuda.synchronize()
+    if not torch.equal(y, eager_y):
+        raise SystemExit("graph replay does not reproduce the eager step")
     s = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(s)
     for i in range(args.steps):
-        ev[i][0].record(s)
-        qt.gemm(x1, gate_up.copies[i % r_steps], out=h)  # the dominant kernel, timed per launch
-        ev[i][1].record(s)
-        qt.gemm(x2, down.copies[i % r_steps], out=y, workspace=ws)
+        graphs[i % r_steps].replay()
     t1.record(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
-    gate_up_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    del graphs
+
+    # The dominant kernel (gate_up): events around each of its launches on
+    # the launch stream, launched eagerly back to back over the copies.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(2 * r_steps)]
+    for i in range(len(ev)):
+        ev[i][0].record(s)
+        qt.gemm(x1, gate_up.copies[i % r_steps], out=h, workspace=ws_g)
+        ev[i][1].record(s)
+    torch.cuda.synchronize()
+    gate_up_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
     achieved = gate_up.bytes_for(m) / (gate_up_us * 1e-6) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us, {value:.0f} GB/s; gate_up {gate_up_us:.1f} us {achieved:.0f} GB/s; "
-        f"wall {wall:.2f} s")
+    log(f"step {ms_step * 1e3:.1f} us, {value:.0f} GB/s; gate_up launch {gate_up_us:.1f} us "
+        f"{achieved:.0f} GB/s; wall {wall:.3f} s")
 
     extras = {}
     if not args.no_extras:
         per = {}
-        per["nvfp4_m1/gate_up"] = time_matrix(gate_up, 1, 40)
-        per["nvfp4_m1/down"] = time_matrix(down, 1, 40)
-        per["nvfp4_m8/gate_up"] = time_matrix(gate_up, 8, 40)
-        per["nvfp4_m8/down"] = time_matrix(down, 8, 40)
+        per["nvfp4_m1/gate_up"] = time_matrix(gate_up, 1)
+        per["nvfp4_m1/down"] = time_matrix(down, 1)
+        per["nvfp4_m8/gate_up"] = time_matrix(gate_up, 8)
+        per["nvfp4_m8/down"] = time_matrix(down, 8)
         del gate_up, down
         torch.cuda.empty_cache()
         for name in ("qkv", "o_proj"):
             mat = Mat(name, "nvfp4", "nvfp4_27b_m8")
-            per[f"nvfp4_m8/{name}"] = time_matrix(mat, 8, 60)
+            per[f"nvfp4_m8/{name}"] = time_matrix(mat, 8)
             del mat
             torch.cuda.empty_cache()
         if args.all:
             for name in ("qkv", "down"):
                 mat = Mat(name, "fp8", "fp8_27b_m124")
                 for mm in (1, 2, 4):
-                    per[f"fp8_m{mm}/{name}"] = time_matrix(mat, mm, 60)
+                    per[f"fp8_m{mm}/{name}"] = time_matrix(mat, mm)
                 del mat
                 torch.cuda.empty_cache()
         for key, (us, gbps) in per.items():

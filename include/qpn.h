@@ -141,7 +141,12 @@ qpn_status qpn_quantize_nvfp4(const float* w_dev, int64_t n, int64_t k, float te
 qpn_status qpn_quantize_fp8(const float* w_dev, int64_t n, int64_t k,
                             uint8_t* codes_dev, float* row_scales_dev, void* stream);
 
-/* Device workspace qpn_gemm needs for this weight and row count (0 if none). */
+/* Device workspace qpn_gemm needs for this weight and row count (0 if none).
+ * When K is split over several workgroups the workspace holds fp32 partial
+ * sums and one arrival counter per group of n-tiles. The counters must be
+ * zero before the first call that uses a workspace (allocate it zeroed);
+ * every call leaves them zero again. Calls that run at the same time must
+ * not share a workspace. */
 size_t qpn_workspace_bytes(const qpn_weight* w, int32_t m);
 
 /*
@@ -152,23 +157,30 @@ size_t qpn_workspace_bytes(const qpn_weight* w, int32_t m);
  *   y_dev     fp16 [m][w->n] row-major output (fully overwritten), 2-byte aligned.
  *   m         0..QPN_MAX_M activation rows (0 or n == 0: nothing to do).
  *   workspace device scratch of at least qpn_workspace_bytes(w, m) bytes
- *             (NULL allowed when that is 0); 16-byte aligned.
+ *             (NULL allowed when that is 0); 16-byte aligned; see above.
  * Accumulation is fp32 over exactly decoded fp16 weights; the result is
  * rounded once to fp16. Deterministic: the same inputs give the same bits.
- * Never synchronizes the stream.
+ * Never synchronizes the stream. Packed weights of 2 GiB or more return
+ * QPN_ERR_UNSUPPORTED.
  */
 qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
                     void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
- * qpn_gemm with an explicit launch shape, for tuning sweeps: split_k > 0
- * splits K into that many ranges (0 = choose automatically) and
- * waves_per_group is 4 or 8 (0 = automatic). The workspace needed for an
- * explicit split is qpn_workspace_bytes_split(w, m, split_k).
+ * qpn_gemm with an explicit launch shape, for tuning sweeps. 0 in any field
+ * means "choose automatically":
+ *   split_k          cut K into this many ranges;
+ *   waves_per_group  4 or 8 wavefronts (n-tiles) per workgroup;
+ *   depth            2, 3, 4, 6 or 8 units of the weight stream in flight per
+ *                    wavefront.
+ * A shape whose activation stage does not fit in LDS returns
+ * QPN_ERR_UNSUPPORTED. The workspace an explicit split needs is
+ * qpn_workspace_bytes_split(w, m, split_k) (0 also when the split is not
+ * possible).
  */
 qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
                           void* workspace_dev, size_t workspace_bytes,
-                          int32_t split_k, int32_t waves_per_group, void* stream);
+                          int32_t split_k, int32_t waves_per_group, int32_t depth, void* stream);
 size_t qpn_workspace_bytes_split(const qpn_weight* w, int32_t m, int32_t split_k);
 
 /*

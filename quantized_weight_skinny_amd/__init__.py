@@ -69,7 +69,7 @@ SIGNATURES = {
     "qpn_workspace_bytes": (_SZ, [_W, _I32]),
     "qpn_workspace_bytes_split": (_SZ, [_W, _I32, _I32]),
     "qpn_gemm": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
-    "qpn_gemm_tuned": (_I32, [_P, _W, _P, _I32, _P, _SZ, _I32, _I32, _P]),
+    "qpn_gemm_tuned": (_I32, [_P, _W, _P, _I32, _P, _SZ, _I32, _I32, _I32, _P]),
     "qpn_read_ceiling": (_I32, [_P, _SZ, _P, _I32, _P]),
     "qpn_read_ceiling_grid": (_I32, []),
 }
@@ -158,9 +158,9 @@ def qpn_gemm(x, weight, y, m, workspace, workspace_bytes, stream):
     return _check(lib().qpn_gemm(x, ctypes.byref(weight), y, m, workspace, workspace_bytes, stream), "qpn_gemm")
 
 
-def qpn_gemm_tuned(x, weight, y, m, workspace, workspace_bytes, split_k, waves_per_group, stream):
+def qpn_gemm_tuned(x, weight, y, m, workspace, workspace_bytes, split_k, waves_per_group, depth, stream):
     return _check(lib().qpn_gemm_tuned(x, ctypes.byref(weight), y, m, workspace, workspace_bytes, split_k,
-                                       waves_per_group, stream), "qpn_gemm_tuned")
+                                       waves_per_group, depth, stream), "qpn_gemm_tuned")
 
 
 def qpn_read_ceiling(buf, nbytes, sink, grid, stream):

@@ -136,7 +136,7 @@ size_t qpn_workspace_bytes_split(const qpn_weight* w, int32_t m, int32_t split_k
   if (check_weight(w) != QPN_OK || m < 0 || m > QPN_MAX_M || split_k < 0) return 0;
   if (m == 0 || w->n == 0) return 0;
   qpn::GemmPlan p;
-  if (!qpn::plan_gemm(w->format, w->n, w->k, m, split_k, 0, &p)) return 0;
+  if (!qpn::plan_gemm(w->format, w->n, w->k, m, split_k, 0, 0, &p)) return 0;
   return p.workspace_bytes;
 }
 
@@ -144,11 +144,13 @@ size_t qpn_workspace_bytes(const qpn_weight* w, int32_t m) { return qpn_workspac
 
 qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
                           void* workspace_dev, size_t workspace_bytes, int32_t split_k,
-                          int32_t waves_per_group, void* stream) {
+                          int32_t waves_per_group, int32_t depth, void* stream) {
   const qpn_status st = check_weight(w);
   if (st != QPN_OK) return st;
   if (m < 0 || m > QPN_MAX_M || split_k < 0) return QPN_ERR_INVALID_ARG;
   if (waves_per_group != 0 && waves_per_group != 4 && waves_per_group != 8) return QPN_ERR_INVALID_ARG;
+  if (depth != 0 && depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8)
+    return QPN_ERR_INVALID_ARG;
   if (m == 0 || w->n == 0) return QPN_OK;
   if (!y_dev || !aligned(y_dev, 2)) return QPN_ERR_INVALID_ARG;
   if (w->k > 0) {
@@ -159,7 +161,7 @@ qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, i
   if (w->format == QPN_FMT_FP8_E4M3 && (!w->row_scales || !aligned(w->row_scales, 4)))
     return QPN_ERR_INVALID_ARG;
   qpn::GemmPlan p;
-  if (!qpn::plan_gemm(w->format, w->n, w->k, m, split_k, waves_per_group, &p))
+  if (!qpn::plan_gemm(w->format, w->n, w->k, m, split_k, waves_per_group, depth, &p))
     return QPN_ERR_UNSUPPORTED;
   if (p.workspace_bytes) {
     if (!workspace_dev || !aligned(workspace_dev, 16)) return QPN_ERR_INVALID_ARG;
@@ -171,7 +173,7 @@ qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, i
 
 qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
                     void* workspace_dev, size_t workspace_bytes, void* stream) {
-  return qpn_gemm_tuned(x_dev, w, y_dev, m, workspace_dev, workspace_bytes, 0, 0, stream);
+  return qpn_gemm_tuned(x_dev, w, y_dev, m, workspace_dev, workspace_bytes, 0, 0, 0, stream);
 }
 
 int32_t qpn_read_ceiling_grid(void) { return qpn::read_ceiling_default_grid(); }

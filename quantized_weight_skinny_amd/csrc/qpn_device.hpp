@@ -4,7 +4,10 @@
 // Packed layout (opaque to callers; produced by the pack kernels).
 // W[N, K] is cut into n-tiles of 16 rows and units of 256 elements along K,
 // padded with zero weights. Tile-unit (nt, u) lives at byte
-// ((nt * KU) + u) * UNIT_BYTES, KU = ceil(K / 256). Lane l of a 64-wide
+// ((u * NT) + nt) * UNIT_BYTES, NT = ceil(N / 16): units are stored K-major,
+// so the wavefronts that stream neighbouring n-tiles in step read one
+// contiguous window of HBM at a time rather than thousands of scattered
+// ones. Lane l of a 64-wide
 // wavefront owns row r = l % 16 of the tile and the 64-element slice
 // k = u*256 + g*64 + [0, 64) with g = l / 16. Its bytes come as 16-byte
 // vectors at stride 1024, so one global_load_dwordx4 per vector brings
@@ -57,27 +60,35 @@ struct Unit<kFmtFp8> {
   u4 q[4];
 };
 
-// A wavefront's slice of the packed stream, read with raw buffer loads: the
-// 64-bit base and the byte range sit in scalar registers, per-lane offsets
-// are 32-bit, and a load past `bytes` returns zeros instead of faulting.
+// Byte offset of tile-unit (nt, u) in a packed buffer with NT n-tiles.
+__host__ __device__ constexpr int64_t unit_offset(int64_t nt, int64_t u, int64_t NT, int64_t unit_bytes) {
+  return (u * NT + nt) * unit_bytes;
+}
+
+// One wavefront's units of one n-tile, read with raw buffer loads: the 64-bit
+// base, the byte range and the unit stride sit in scalar registers, per-lane
+// offsets are 32-bit, and a load past `bytes` returns zeros instead of
+// faulting.
 struct Stream {
   __amdgpu_buffer_rsrc_t rsrc;
-  __device__ __forceinline__ Stream(const uint8_t* base, uint32_t bytes)
-      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kRsrcWord3)) {}
+  uint32_t stride;  // bytes from one unit of the tile to the next
+  __device__ __forceinline__ Stream(const uint8_t* base, uint32_t bytes, uint32_t unit_stride)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kRsrcWord3)),
+        stride(unit_stride) {}
   static constexpr int kRsrcWord3 = 0x00020000;
   static constexpr int kStreaming = 2;  // nt: the weights are read once
 };
 
-// Streaming loads of unit `u` of the slice for this lane.
+// Streaming loads of unit `u` (counted from the stream's first unit).
 __device__ __forceinline__ void load_unit(Unit<kFmtNvfp4>& r, const Stream& s, int u, int lane) {
-  const int base = u * kNvUnitBytes;
+  const int base = u * s.stride;
   r.c0 = __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, lane * 16, base, Stream::kStreaming);
   r.c1 = __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, lane * 16 + 1024, base, Stream::kStreaming);
   r.sc = __builtin_amdgcn_raw_buffer_load_b32(s.rsrc, lane * 4 + 2048, base, Stream::kStreaming);
 }
 
 __device__ __forceinline__ void load_unit(Unit<kFmtFp8>& r, const Stream& s, int u, int lane) {
-  const int base = u * kF8UnitBytes;
+  const int base = u * s.stride;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     r.q[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, lane * 16 + q * 1024, base, Stream::kStreaming);

@@ -10,18 +10,21 @@ namespace qpn {
 // Launch plan of one GEMM call: the K range is cut into `split` pieces of
 // `units_per_split` 256-element units; each workgroup of `waves` wavefronts
 // handles `waves` n-tiles of one piece. split > 1 writes fp32 partial sums to
-// the workspace and a second kernel adds them in piece order.
+// the workspace; the last workgroup of a group to finish adds them in piece
+// order.
 struct GemmPlan {
   int split;
   int waves;
+  int depth;       // units of the weight stream each wavefront keeps in flight
   int units_per_split;
   int lds_stride;  // halves per staged activation row
   size_t lds_bytes;
-  size_t workspace_bytes;
+  size_t partials_offset;  // the workspace holds per-group arrival counters, then
+  size_t workspace_bytes;  // fp32 partials [split][m][n] from this offset (0 if split == 1)
 };
 
 bool plan_gemm(int fmt, int64_t n, int64_t k, int m, int split_override, int waves_override,
-               GemmPlan* plan);
+               int depth_override, GemmPlan* plan);
 
 hipError_t launch_gemm(int fmt, const GemmPlan& plan, const void* x, const void* packed,
                        const float* row_scales, float tensor_scale, void* y, void* workspace,

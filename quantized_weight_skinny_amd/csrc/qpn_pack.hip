@@ -40,7 +40,7 @@ __device__ __forceinline__ int count_nan_e4m3(uint32_t w, int nbytes) {
 // One thread per 32-code chunk (16 bytes) of a padded row.
 __global__ __launch_bounds__(kBlock) void pack_nvfp4_codes(const uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ packed, int64_t N,
-                                                           int64_t K, int64_t KU, int64_t total) {
+                                                           int64_t K, int64_t NT, int64_t KU, int64_t total) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (idx >= total) return;
   const int64_t n = idx / (KU * 8);
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kBlock) void pack_nvfp4_codes(const uint8_t* __rest
   const int64_t k0 = c * 32;
   const int64_t u = c >> 3, g = (c >> 1) & 3, h = c & 1;
   const int64_t nt = n >> 4, r = n & 15;
-  uint8_t* dst = packed + (nt * KU + u) * kNvUnitBytes + h * 1024 + (g * 16 + r) * 16;
+  uint8_t* dst = packed + unit_offset(nt, u, NT, kNvUnitBytes) + h * 1024 + (g * 16 + r) * 16;
   int nbytes = 0;
   if (n < N && k0 < K) nbytes = static_cast<int>((K - k0) / 2 < 16 ? (K - k0) / 2 : 16);
   const uint4 v = load16_bytes(codes + n * (K / 2) + k0 / 2, nbytes);
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kBlock) void pack_nvfp4_codes(const uint8_t* __rest
 // One thread per group of 4 block scales (64 elements) of a padded row.
 __global__ __launch_bounds__(kBlock) void pack_nvfp4_scales(const uint8_t* __restrict__ scales,
                                                             uint8_t* __restrict__ packed, int64_t N,
-                                                            int64_t K, int64_t KU, int64_t total,
+                                                            int64_t K, int64_t NT, int64_t KU, int64_t total,
                                                             int32_t* __restrict__ bad) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (idx >= total) return;
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kBlock) void pack_nvfp4_scales(const uint8_t* __res
       }
     }
   }
-  *reinterpret_cast<uint32_t*>(packed + (nt * KU + u) * kNvUnitBytes + 2048 + (g * 16 + r) * 4) = w;
+  *reinterpret_cast<uint32_t*>(packed + unit_offset(nt, u, NT, kNvUnitBytes) + 2048 + (g * 16 + r) * 4) = w;
   if (bad) {
     const int nb = count_nan_e4m3(w, nvalid);
     if (nb) atomicAdd(bad, nb);
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void pack_nvfp4_scales(const uint8_t* __res
 // One thread per 16-code chunk of a padded row.
 __global__ __launch_bounds__(kBlock) void pack_fp8_codes(const uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ packed, int64_t N,
-                                                         int64_t K, int64_t KU, int64_t total,
+                                                         int64_t K, int64_t NT, int64_t KU, int64_t total,
                                                          int32_t* __restrict__ bad) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (idx >= total) return;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kBlock) void pack_fp8_codes(const uint8_t* __restri
   const int64_t k0 = c * 16;
   const int64_t u = c >> 4, g = (c >> 2) & 3, q = c & 3;
   const int64_t nt = n >> 4, r = n & 15;
-  uint8_t* dst = packed + (nt * KU + u) * kF8UnitBytes + q * 1024 + (g * 16 + r) * 16;
+  uint8_t* dst = packed + unit_offset(nt, u, NT, kF8UnitBytes) + q * 1024 + (g * 16 + r) * 16;
   const int nbytes = (n < N && k0 < K) ? 16 : 0;
   const uint4 v = load16_bytes(codes + n * K + k0, nbytes);
   *reinterpret_cast<uint4*>(dst) = v;
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(kBlock) void pack_fp8_codes(const uint8_t* __restri
 __global__ __launch_bounds__(kBlock) void unpack_nvfp4_kernel(const uint8_t* __restrict__ packed,
                                                               uint8_t* __restrict__ codes,
                                                               uint8_t* __restrict__ scales,
-                                                              int64_t N, int64_t K, int64_t KU,
-                                                              int64_t total) {
+                                                              int64_t N, int64_t K, int64_t NT,
+                                                              int64_t KU, int64_t total) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (idx >= total) return;
   const int64_t n = idx / (KU * 8);
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kBlock) void unpack_nvfp4_kernel(const uint8_t* __r
   if (k0 >= K) return;
   const int64_t u = c >> 3, g = (c >> 1) & 3, h = c & 1;
   const int64_t nt = n >> 4, r = n & 15;
-  const uint8_t* unit = packed + (nt * KU + u) * kNvUnitBytes;
+  const uint8_t* unit = packed + unit_offset(nt, u, NT, kNvUnitBytes);
   const uint4 v = *reinterpret_cast<const uint4*>(unit + h * 1024 + (g * 16 + r) * 16);
   const int nbytes = static_cast<int>((K - k0) / 2 < 16 ? (K - k0) / 2 : 16);
   store16_bytes(codes + n * (K / 2) + k0 / 2, v, nbytes);
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kBlock) void unpack_nvfp4_kernel(const uint8_t* __r
 
 __global__ __launch_bounds__(kBlock) void unpack_fp8_kernel(const uint8_t* __restrict__ packed,
                                                             uint8_t* __restrict__ codes, int64_t N,
-                                                            int64_t K, int64_t KU, int64_t total) {
+                                                            int64_t K, int64_t NT, int64_t KU, int64_t total) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (idx >= total) return;
   const int64_t n = idx / (KU * 16);
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kBlock) void unpack_fp8_kernel(const uint8_t* __res
   if (k0 >= K) return;
   const int64_t u = c >> 4, g = (c >> 2) & 3, q = c & 3;
   const int64_t nt = n >> 4, r = n & 15;
-  const uint4 v = *reinterpret_cast<const uint4*>(packed + (nt * KU + u) * kF8UnitBytes + q * 1024 +
+  const uint4 v = *reinterpret_cast<const uint4*>(packed + unit_offset(nt, u, NT, kF8UnitBytes) + q * 1024 +
                                                   (g * 16 + r) * 16);
   store16_bytes(codes + n * K + k0, v, 16);
 }
@@ -260,10 +260,10 @@ hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_
   const int64_t rows = NT * kTileN;
   const int64_t t1 = rows * KU * 8;
   hipLaunchKernelGGL(pack_nvfp4_codes, dim3(blocks_for(t1)), dim3(kBlock), 0, stream, codes,
-                     static_cast<uint8_t*>(packed), n, k, KU, t1);
+                     static_cast<uint8_t*>(packed), n, k, NT, KU, t1);
   const int64_t t2 = rows * KU * 4;
   hipLaunchKernelGGL(pack_nvfp4_scales, dim3(blocks_for(t2)), dim3(kBlock), 0, stream, scales,
-                     static_cast<uint8_t*>(packed), n, k, KU, t2, bad);
+                     static_cast<uint8_t*>(packed), n, k, NT, KU, t2, bad);
   return hipGetLastError();
 }
 
@@ -273,27 +273,27 @@ hipError_t launch_pack_fp8(const uint8_t* codes, int64_t n, int64_t k, void* pac
   if (NT == 0 || KU == 0) return hipSuccess;
   const int64_t t = NT * kTileN * KU * 16;
   hipLaunchKernelGGL(pack_fp8_codes, dim3(blocks_for(t)), dim3(kBlock), 0, stream, codes,
-                     static_cast<uint8_t*>(packed), n, k, KU, t, bad);
+                     static_cast<uint8_t*>(packed), n, k, NT, KU, t, bad);
   return hipGetLastError();
 }
 
 hipError_t launch_unpack_nvfp4(const void* packed, int64_t n, int64_t k, uint8_t* codes,
                                uint8_t* scales, hipStream_t stream) {
-  const int64_t KU = ceil_div(k, kUnitK);
+  const int64_t NT = ceil_div(n, kTileN), KU = ceil_div(k, kUnitK);
   if (n == 0 || KU == 0) return hipSuccess;
   const int64_t t = n * KU * 8;
   hipLaunchKernelGGL(unpack_nvfp4_kernel, dim3(blocks_for(t)), dim3(kBlock), 0, stream,
-                     static_cast<const uint8_t*>(packed), codes, scales, n, k, KU, t);
+                     static_cast<const uint8_t*>(packed), codes, scales, n, k, NT, KU, t);
   return hipGetLastError();
 }
 
 hipError_t launch_unpack_fp8(const void* packed, int64_t n, int64_t k, uint8_t* codes,
                              hipStream_t stream) {
-  const int64_t KU = ceil_div(k, kUnitK);
+  const int64_t NT = ceil_div(n, kTileN), KU = ceil_div(k, kUnitK);
   if (n == 0 || KU == 0) return hipSuccess;
   const int64_t t = n * KU * 16;
   hipLaunchKernelGGL(unpack_fp8_kernel, dim3(blocks_for(t)), dim3(kBlock), 0, stream,
-                     static_cast<const uint8_t*>(packed), codes, n, k, KU, t);
+                     static_cast<const uint8_t*>(packed), codes, n, k, NT, KU, t);
   return hipGetLastError();
 }
 

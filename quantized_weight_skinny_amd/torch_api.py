@@ -153,8 +153,17 @@ def workspace_bytes(pw, m, split_k=0):
     return qpn_workspace_bytes_split(d, m, split_k) if split_k else qpn_workspace_bytes(d, m)
 
 
-def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0):
-    """y[m, n] = x[m, k] @ dequant(W)^T in fp16 through qpn_gemm."""
+def new_workspace(pw, m, split_k=0, device="cuda"):
+    """A zeroed workspace for gemm(pw) with m rows (None when none is needed)."""
+    need = workspace_bytes(pw, m, split_k)
+    return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
+
+
+def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0):
+    """y[m, n] = x[m, k] @ dequant(W)^T in fp16 through qpn_gemm.
+
+    A workspace, when one is needed and not given, is allocated zeroed per
+    call; pass one from new_workspace() to reuse it across calls."""
     _cuda(x, torch.float16, "x")
     m = x.shape[0]
     if out is None:
@@ -162,11 +171,11 @@ def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0):
     d = pw.desc()
     need = qpn_workspace_bytes_split(d, m, split_k) if split_k else qpn_workspace_bytes(d, m)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if need else 0
-    if split_k or waves:
-        qpn_gemm_tuned(x.data_ptr(), d, out.data_ptr(), m, ws_ptr, ws_bytes, split_k, waves, _stream())
+    if split_k or waves or depth:
+        qpn_gemm_tuned(x.data_ptr(), d, out.data_ptr(), m, ws_ptr, ws_bytes, split_k, waves, depth, _stream())
     else:
         qpn_gemm(x.data_ptr(), d, out.data_ptr(), m, ws_ptr, ws_bytes, _stream())
     return out

@@ -61,8 +61,8 @@ def _w(fmt=q.QPN_FMT_NVFP4, n=512, k=1024, packed=FAKE, rs=FAKE):
     return q.make_weight(fmt, n, k, packed, 1.0, rs)
 
 
-def _gemm(x, w, y, m, ws=None, wsb=0, split=0, waves=0):
-    return q.lib().qpn_gemm_tuned(x, ctypes.byref(w), y, m, ws, wsb, split, waves, None)
+def _gemm(x, w, y, m, ws=None, wsb=0, split=0, waves=0, depth=0):
+    return q.lib().qpn_gemm_tuned(x, ctypes.byref(w), y, m, ws, wsb, split, waves, depth, None)
 
 
 def test_gemm_rejects_bad_arguments_before_any_device_call():
@@ -78,6 +78,7 @@ def test_gemm_rejects_bad_arguments_before_any_device_call():
     assert _gemm(FAKE, _w(fmt=9), FAKE, 1) == err             # format
     assert _gemm(FAKE, _w(fmt=q.QPN_FMT_FP8_E4M3, rs=None), FAKE, 1) == err  # FP8 needs row scales
     assert _gemm(FAKE, _w(), FAKE, 1, waves=5) == err
+    assert _gemm(FAKE, _w(), FAKE, 1, depth=5) == err
     w = _w()
     w.reserved = 1
     assert _gemm(FAKE, w, FAKE, 1) == err
@@ -96,7 +97,9 @@ def test_gemm_workspace_checks():
     assert need > 0                                           # small N splits K
     assert _gemm(FAKE, w, FAKE, 8, None, 0) == q.QPN_ERR_INVALID_ARG
     assert _gemm(FAKE, w, FAKE, 8, FAKE, need - 16) == q.QPN_ERR_BUFFER_TOO_SMALL
-    assert q.qpn_workspace_bytes_split(w, 8, 5) == 5 * 8 * 5120 * 4
+    # one counter per group of 4 n-tiles (padded to 256 bytes), then fp32 partials [split][m][n]
+    counters = (5120 // 16 // 4) * 4
+    assert q.qpn_workspace_bytes_split(w, 8, 5) == (counters + 255) // 256 * 256 + 5 * 8 * 5120 * 4
     # one K range of 17408 x 8 rows does not fit the activation stage in LDS
     assert q.qpn_workspace_bytes_split(w, 8, 1) == 0
     assert _gemm(FAKE, w, FAKE, 8, FAKE, need, split=1) == q.QPN_ERR_UNSUPPORTED

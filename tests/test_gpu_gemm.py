@@ -38,11 +38,36 @@ def test_gemm_parity_small(fmt, m, n, k):
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
-@pytest.mark.parametrize("split,waves", [(1, 4), (2, 4), (3, 8), (5, 4), (7, 8), (0, 8)])
-def test_gemm_launch_shapes_agree(fmt, split, waves):
+@pytest.mark.parametrize("split,waves,depth", [(1, 4, 2), (2, 4, 3), (3, 8, 4), (5, 4, 6), (7, 8, 8),
+                                               (0, 8, 0), (4, 4, 8), (1, 8, 6)])
+def test_gemm_launch_shapes_agree(fmt, split, waves, depth):
     n, k, m = 96, 1792, 5
-    say("gemm tuned", fmt, split, waves)
-    _parity(fmt, m, n, k, seed=77, split_k=split, waves=waves)
+    say("gemm tuned", fmt, split, waves, depth)
+    _parity(fmt, m, n, k, seed=77, split_k=split, waves=waves, depth=depth)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_split_k_workspace_reuse_is_deterministic(fmt):
+    """The split-K arrival counters are left at zero by every call, so one
+    workspace serves many calls (and different row counts) with identical bits."""
+    n, k = 5120, 17408 // 4
+    say("split-k reuse", fmt)
+    w = workloads.weights(n, k, 21)
+    pw, _ = gpu_quantize(fmt, to_dev(w))
+    ws = qt.new_workspace(pw, 16, split_k=6)
+    assert ws is not None
+    outs = []
+    for m in (8, 3, 8, 16, 8):
+        x = to_dev(workloads.activations(m, k, 22)[:m])
+        outs.append((m, to_host(qt.gemm(x, pw, workspace=ws, split_k=6))))
+    assert not to_host(ws[:(n // 16 // 4) * 4]).any()  # counters back at zero
+    ref8 = outs[0][1]
+    for m, y in outs:
+        if m == 8:
+            assert np.array_equal(y.view(np.uint16), ref8.view(np.uint16))
+    parts = oracle_quantize(fmt, w)
+    y_ref, b = oracle_y(fmt, workloads.activations(16, k, 22), parts)
+    assert_within_tolerance(outs[3][1], y_ref, b, f"{fmt} split 6 m=16")
 
 
 def test_gemm_vs_hand_case():

@@ -124,13 +124,13 @@ def test_pack_unpack_nvfp4_round_trip(n, k):
     # every padding byte (rows past n, columns past k) is zero
     raw = to_host(pw.packed)
     nt, ku = -(-n // 16), -(-k // 256)
-    units = raw.reshape(nt, ku, 2304)
+    units = raw.reshape(ku, nt, 2304)  # K-unit-major: unit u of every n-tile, then u + 1
     lane = np.arange(64)
     r, g = lane % 16, lane // 16
     for t in range(nt):
         for u in range(ku):
             for h in range(2):
-                vec = units[t, u, h * 1024:(h + 1) * 1024].reshape(64, 16)
+                vec = units[u, t, h * 1024:(h + 1) * 1024].reshape(64, 16)
                 row = t * 16 + r
                 k0 = u * 256 + g * 64 + h * 32
                 dead = (row >= n) | (k0 >= k)
