@@ -149,6 +149,69 @@ def read_ceiling(nbytes=4 << 30, reps=6):
     return best
 
 
+def read_ceiling_sized(nbytes, total=4 << 30, reps=2):
+    """Read-kernel bandwidth when each launch reads one matrix-sized slice of
+    a large buffer (rotating slices, graph of back-to-back launches)."""
+    import torch
+    from quantized_weight_skinny_amd import torch_api as qt
+    from quantized_weight_skinny_amd import qpn_read_ceiling_grid
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    size = (nbytes + 15) // 16 * 16
+    slices = [buf[i * size:(i + 1) * size] for i in range(total // size)]
+    grid = qpn_read_ceiling_grid() // 4
+    sink = torch.empty(grid * 4, dtype=torch.int32, device="cuda")
+    g = capture([(lambda sl=sl: qt.read_ceiling(sl, grid, sink)) for sl in slices])
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(slices))
+    del g, buf
+    torch.cuda.empty_cache()
+    return size / (us * 1e-6) / 1e9
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources the GEMM kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_weight_skinny_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nvfp4_gate_up_m1_traffic.md")
+
+
+def kernel_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None when the kernel sources changed after
+    the counters were taken (the summary records the source hash)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel source sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(rows):
     """The oracle (numpy, float64 dequantize then matmul) on a bounded sample:
     the first ``rows`` rows of gate_up and of down at M=1, repeated to about
@@ -218,18 +281,16 @@ def main():
         qt.gemm(x1, gate_up.copies[i % r_steps], out=h, workspace=ws_g)
         qt.gemm(x2, down.copies[i % r_steps], out=y, workspace=ws_d)
 
-    # One graph per rotating copy, each holding one step (gate_up then down):
-    # the timed loop replays exactly `steps` graphs, so no Python launch
-    # overhead sits between the kernels.
+    # The warmup and the timed steps are each one HIP graph (W and K steps,
+    # cycling through the rotating copies), so no Python launch overhead
+    # sits between the kernels; the graph is checked against the eager step.
     for i in range(r_steps):
         step(i)
     torch.cuda.synchronize()
     eager_y = y.clone()
-    graphs = [capture([lambda i=i: step(i)]) for i in range(r_steps)]
-    for i in range(args.warmup):
-        graphs[i % r_steps].replay()
-    torch.cuda.synchronize()
-    graphs[(r_steps - 1)].replay()
+    warm = capture([(lambda i=i: step(i)) for i in range(max(args.warmup, 1))])
+    timed = capture([(lambda i=i: step(i)) for i in range(args.steps)])
+    warm.replay()
     torch.cuda.synchronize()
     if not torch.equal(y, eager_y):
         raise SystemExit("graph replay does not reproduce the eager step")
@@ -238,28 +299,25 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(s)
-    for i in range(args.steps):
-        graphs[i % r_steps].replay()
+    timed.replay()
     t1.record(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    del graphs
+    del warm, timed
 
-    # The dominant kernel (gate_up): events around each of its launches on
-    # the launch stream, launched eagerly back to back over the copies.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(2 * r_steps)]
-    for i in range(len(ev)):
-        ev[i][0].record(s)
-        qt.gemm(x1, gate_up.copies[i % r_steps], out=h, workspace=ws_g)
-        ev[i][1].record(s)
-    torch.cuda.synchronize()
-    gate_up_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
-    achieved = gate_up.bytes_for(m) / (gate_up_us * 1e-6) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us, {value:.0f} GB/s; gate_up launch {gate_up_us:.1f} us "
-        f"{achieved:.0f} GB/s; wall {wall:.3f} s")
+    # The dominant kernel (gate_up): a graph of back-to-back launches over
+    # the rotating copies, events on the launch stream around it.
+    gate_up_us, achieved = time_matrix(gate_up, m, reps=2)
+    traffic = kernel_traffic()
+    log(f"step {ms_step * 1e3:.1f} us, {value:.0f} GB/s; gate_up {gate_up_us:.1f} us per launch, "
+        f"{achieved:.0f} GB/s; wall {wall:.3f} s; traffic {traffic}")
+
+    # Same-size ceiling: the read kernel over 100 MB slices of a rotating
+    # buffer, the size of one gate_up launch.
+    same_size = read_ceiling_sized(gate_up.weight_bytes)
+    log(f"read ceiling at gate_up size: {same_size:.0f} GB/s")
 
     extras = {}
     if not args.no_extras:
@@ -314,9 +372,11 @@ def main():
         "config": {"workload": "nvfp4_27b_m1: NVFP4 gate_up 34816x5120 + down 5120x17408, M=1",
                    "m": 1, "format": "nvfp4", "rotating_copies": r_steps, "step_bytes": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "gemm_kernel<NVFP4> on gate_up 34816x5120, M=1"},
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "kernel": "gemm_kernel<NVFP4> on gate_up 34816x5120, M=1",
+                     "launch_us": round(gate_up_us, 3), "algorithmic_bytes": gate_up.bytes_for(m)},
         "measured_read_ceiling_GBps": round(ceiling, 1),
+        "read_ceiling_at_gate_up_size_GBps": round(same_size, 1),
         "frac_of_measured_ceiling": round(value / ceiling, 4),
         "cpu_baseline": cpu,
         "per_matrix": extras,

@@ -44,12 +44,20 @@ constexpr int kFmtFp8 = 2;
 
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// s_waitcnt immediate that waits until at most n vector memory operations
+// are outstanding and leaves the other counters alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// ... and the same for the LDS / scalar-memory counter (vmcnt left at 63).
+constexpr int lgkmcnt_only(int n) { return 15 | (3 << 14) | (7 << 4) | ((n & 15) << 8); }
+
 template <int FMT>
 struct Unit;
 
 template <>
 struct Unit<kFmtNvfp4> {
   static constexpr int kBytes = kNvUnitBytes;
+  static constexpr int kLoads = 3;  // vector memory instructions per unit
   u4 c0, c1;
   uint32_t sc;
 };
@@ -57,6 +65,7 @@ struct Unit<kFmtNvfp4> {
 template <>
 struct Unit<kFmtFp8> {
   static constexpr int kBytes = kF8UnitBytes;
+  static constexpr int kLoads = 4;
   u4 q[4];
 };
 

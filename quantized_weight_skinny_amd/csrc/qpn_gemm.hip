@@ -29,8 +29,31 @@ namespace qpn {
 namespace {
 
 constexpr size_t kLdsBudget = 64 * 1024;
-constexpr int kTargetWaves = 2048;  // about 8 wavefronts per CU on 256 CUs
+// Launch-shape heuristic, from a sweep of split x waves x depth on MI355X
+// over the 27B shapes (N-tiles 320..9496, K units 20..68, M 1..8): the best
+// split puts about 960 wavefronts (n-tiles x K ranges) on the chip, a
+// stream depth of 3 units is within noise of the best everywhere, and
+// 8-wave workgroups only pay off on very wide matrices.
+constexpr int kTargetWaves = 960;
+constexpr int kWideTiles = 4096;
 constexpr int kRowPad = 8;          // fp16 pad per staged row (bank spread)
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Direct-to-LDS load of 16 bytes per lane: lane i's bytes land at LDS byte
+// address lds_base + 16 * i (lds_base is wave-uniform and goes through M0).
+// Written as inline assembly so that the compiler's wait-count bookkeeping
+// does not see an LDS write in flight: left to itself it makes every later
+// LDS read wait for all outstanding loads, the weight stream included. The
+// caller waits for these loads explicitly before the workgroup barrier.
+// (Untracked older loads can only make the compiler's own waits stricter,
+// since the counter retires loads in issue order.)
+__device__ __forceinline__ void lds_dma16(const void* src, _Float16* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds_dst))));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ h8 x_fragment(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
 
@@ -60,7 +83,7 @@ __device__ __forceinline__ void unit_mfma(const Unit<kFmtFp8>& w, const _Float16
 
 template <int FMT, int WAVES, int DEPTH>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
-    const _Float16* __restrict__ x, const uint8_t* __restrict__ packed,
+    const _Float16* __restrict__ x, const uint8_t* packed,
     const float* __restrict__ row_scales, float tensor_scale, _Float16* __restrict__ y,
     float* __restrict__ ws, int* __restrict__ counters, int M, int N, int K, int NT, int KU, int ups,
     int stride) {
@@ -81,31 +104,54 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
                       active && nu > 0 ? static_cast<uint32_t>(nu - 1) * unit_stride + kBytes : 0u,
                       unit_stride);
 
-  // Issue the first DEPTH units unit by unit, in the order the loop will
-  // consume them, so that the wait before each unit counts only its own loads.
+  // Stage this K range of every activation row in LDS with direct-to-LDS
+  // loads: one global_load_lds_dwordx4 moves 64 lanes x 16 B (two units of
+  // one row) without passing through registers, so all of them can be in
+  // flight at once. Chunks past K (the zero-padded tail of the last unit)
+  // are written as zeros first, so that 0 * x stays finite; lanes past the
+  // row's staged length are masked off.
+  const int row_chunks = nu * (kUnitK / 8);
+  const int kbase = u0 * kUnitK;
+  const int live_chunks = min(row_chunks, max(0, (K - kbase) / 8));
+  if (live_chunks < row_chunks) {
+    const int tail = row_chunks - live_chunks;
+    for (int idx = tid; idx < M * tail; idx += WAVES * 64) {
+      const int m = idx / tail;
+      *reinterpret_cast<uint4*>(xs + m * stride + (live_chunks + idx - m * tail) * 8) =
+          make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  const int windows = (live_chunks + 63) / 64;
+  for (int wi = wave; wi < M * windows; wi += WAVES) {
+    const int m = wi / windows;
+    const int c0 = (wi - m * windows) * 64;
+    if (c0 + lane < live_chunks)
+      lds_dma16(x + static_cast<size_t>(m) * K + kbase + (c0 + lane) * 8, xs + m * stride + c0 * 8);
+  }
+
+  // Then issue the first DEPTH units of the weight stream unit by unit, in
+  // the order the loop will consume them. (`packed` is deliberately not
+  // __restrict__: with it the compiler may treat the weights as immutable and
+  // sink these loads past the barrier below, which would both delay the
+  // stream and break the staging wait.) Loads are never conditional: a
+  // unit past the wavefront's range lies past the stream's byte range, so
+  // the buffer load returns zeros without touching memory. This keeps the
+  // compiler's view of in-flight loads exact at every point.
   Unit<FMT> buf[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
-    if (i < nu) load_unit(buf[i], stream, i, lane);
-    __builtin_amdgcn_sched_barrier(0);
+    load_unit(buf[i], stream, i, lane);
+    asm volatile("" ::: "memory");  // keep the units' loads in this order
   }
-
-  // Stage this K range of every activation row in LDS, zero past K.
-  const int chunks = nu * (kUnitK / 8);
-  const int kbase = u0 * kUnitK;
-  for (int idx = tid; idx < M * chunks; idx += WAVES * 64) {
-    const int m = idx / chunks;
-    const int c = idx - m * chunks;
-    const int kk = kbase + c * 8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (kk < K) v = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(m) * K + kk);
-    *reinterpret_cast<uint4*>(xs + m * stride + c * 8) = v;
-  }
-  __syncthreads();
-  // Settle every load issued so far (the first units and the staging reads):
-  // the loop below then starts from a known queue of in-flight loads and
-  // each unit waits only for its own.
-  __builtin_amdgcn_s_waitcnt(0);
+  // Wait for the staging loads only (they were issued before the weight
+  // loads, and the counter retires loads in order) and for the zero stores,
+  // then meet at a bare barrier: the weight loads stay in flight across it.
+  // (A full __syncthreads would also wait for them.)
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(Unit<FMT>::kLoads * DEPTH));
+  __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
   // B-operand column m of the MFMA is activation row m. Lanes of columns
   // m >= M read row M-1 (an LDS broadcast); their output columns are never
@@ -116,31 +162,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   f4 acc = {0.f, 0.f, 0.f, 0.f};
 
   if (active) {
-    // Each slot of buf is consumed and then refilled in place, so the loop
-    // carries no register copies and keeps DEPTH-1 units in flight while it
-    // computes. The steady-state loop has no conditional loads; the last
-    // (< 2*DEPTH) units run as straight-line code.
-    int u = 0;
-    for (; u + 2 * DEPTH <= nu; u += DEPTH) {
+    // Each slot of buf is consumed and then refilled in place (unit u + DEPTH
+    // goes where unit u was), so the loop carries no register copies and
+    // keeps DEPTH-1 units in flight while it computes. Refills past the end
+    // of the range read zeros and cost no memory traffic.
+    for (int base = 0; base < nu; base += DEPTH) {
 #pragma unroll
       for (int i = 0; i < DEPTH; ++i) {
-        unit_mfma(buf[i], xrow + (u + i) * kUnitK, acc);
-        load_unit(buf[i], stream, u + DEPTH + i, lane);
+        if (base + i < nu) unit_mfma(buf[i], xrow + (base + i) * kUnitK, acc);
+        load_unit(buf[i], stream, base + DEPTH + i, lane);
         // keep the scheduler from sinking the refill below the next units' math
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-#pragma unroll
-    for (int i = 0; i < DEPTH; ++i) {
-      if (u + i < nu) {
-        unit_mfma(buf[i], xrow + (u + i) * kUnitK, acc);
-        if (u + DEPTH + i < nu) load_unit(buf[i], stream, u + DEPTH + i, lane);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < DEPTH; ++i)
-      if (u + DEPTH + i < nu) unit_mfma(buf[i], xrow + (u + DEPTH + i) * kUnitK, acc);
   }
 
   // Lane (m = lane % 16, g = lane / 16) holds rows n = 4g + r of column m.
@@ -165,18 +199,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   // adds all ranges in range order (the same order whichever arrives last, so
   // the result is deterministic) and resets the group's counter for the next
   // call. No workgroup ever waits for another.
+  //
+  // Partials and counters are accessed only through relaxed device-scope
+  // atomics, which on gfx950 are plain loads and stores that bypass the
+  // per-XCD L2 to the device-coherent level (sc1), so no cache-wide
+  // writeback or invalidate is needed. Ordering comes from completion: each
+  // thread waits for its partial stores to be acknowledged before the
+  // workgroup barrier that precedes the counter increment, and the last
+  // workgroup issues its loads only after the increment has returned.
   if (active && mcol < M) {
     float* dst = ws + (static_cast<size_t>(s) * M + mcol) * N;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (n0 + r < N) dst[n0 + r] = acc[r];
+      if (n0 + r < N) __hip_atomic_store(dst + n0 + r, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) last_group = atomicAdd(counters + blockIdx.x, 1) == S - 1;
+  if (tid == 0)
+    last_group = __hip_atomic_fetch_add(counters + blockIdx.x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 S - 1;
   __syncthreads();
   if (!last_group) return;
-  __threadfence();
   const int rows = WAVES * kTileN;
   const int nbase = blockIdx.x * rows;
   for (int idx = tid; idx < M * rows; idx += WAVES * 64) {
@@ -185,11 +228,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     if (n >= N) continue;
     const float* src = ws + static_cast<size_t>(m) * N + n;
     float sum = 0.f;
-    for (int r = 0; r < S; ++r) sum += src[static_cast<size_t>(r) * M * N];
+    for (int r = 0; r < S; ++r)
+      sum += __hip_atomic_load(src + static_cast<size_t>(r) * M * N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float scale = FMT == kFmtNvfp4 ? tensor_scale : row_scales[n];
     y[static_cast<size_t>(m) * N + n] = static_cast<_Float16>(sum * scale);
   }
-  if (tid == 0) atomicExch(counters + blockIdx.x, 0);
+  if (tid == 0) __hip_atomic_store(counters + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int FMT, int WAVES, int DEPTH>
@@ -229,11 +273,11 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, int split_override, int wav
                int depth_override, GemmPlan* p) {
   if (fmt != kFmtNvfp4 && fmt != kFmtFp8) return false;
   if (m < 1 || m > kMaxM || n < 1 || k < 0) return false;
-  const int waves = waves_override ? waves_override : 4;
-  if (waves != 4 && waves != 8) return false;
-  const int depth = depth_override ? depth_override : (fmt == kFmtNvfp4 ? 4 : 2);
-  if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
   const int64_t NT = ceil_div(n, kTileN);
+  const int waves = waves_override ? waves_override : (NT >= kWideTiles ? 8 : 4);
+  if (waves != 4 && waves != 8) return false;
+  const int depth = depth_override ? depth_override : 3;
+  if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
   const int64_t KU = ceil_div(k, kUnitK);
   const int64_t unit_bytes = fmt == kFmtNvfp4 ? kNvUnitBytes : kF8UnitBytes;
   // unit offsets inside one wavefront's stream are 32-bit
@@ -244,7 +288,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, int split_override, int wav
     split = split_override;
   } else {
     const int64_t s_lds = KU ? ceil_div(KU, max_ups) : 1;
-    const int64_t s_occ = ceil_div(kTargetWaves, NT);
+    const int64_t s_occ = (kTargetWaves + NT / 2) / NT;  // nearest
     split = s_lds > s_occ ? s_lds : s_occ;
   }
   if (split > KU) split = KU ? KU : 1;
