@@ -176,15 +176,18 @@ def read_ceiling_sized(nbytes, total=4 << 30, reps=2):
     return size / (us * 1e-6) / 1e9
 
 
+KERNEL_SOURCES = ("qpn_device.hpp", "qpn_gemm.hip", "qpn_internal.hpp")
+
+
 def kernel_source_hash():
-    """sha256 over the HIP sources the GEMM kernel is built from."""
+    """sha256 over the sources that define the GEMM kernel and its launch
+    plan (the C-ABI wrapper and the offline kernels do not enter it)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_weight_skinny_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
@@ -210,6 +213,57 @@ def kernel_traffic():
         return int(fields["traffic bytes per launch"])
     except (KeyError, ValueError):
         return None
+
+
+def decode_step(ms=(1, 2, 4, 8), reps=3):
+    """The synthetic decode step of a ~27B dense decoder: 64 layers of
+    [qkv FP8, o_proj FP8, gate_up NVFP4, down NVFP4], then the NVFP4 lm_head,
+    each layer's weights at their own addresses (14.1 GB in all), launched in
+    order as one HIP graph. Returns {m: (ms per step, aggregate GB/s)}."""
+    import torch
+    from quantized_weight_skinny_amd import torch_api as qt
+    wl = "decode_step_27b"
+    protos = {}
+    for name, fmt in workloads.DECODE_LAYER_MATS:
+        protos[name] = Mat(name, fmt, wl, copies=workloads.DECODE_LAYERS)
+    head = Mat("lm_head", "nvfp4", wl, copies=1)
+    out = {}
+    for m in ms:
+        launches, total = [], 0
+        bufs = {}
+        for name, _ in workloads.DECODE_LAYER_MATS + (("lm_head", "nvfp4"),):
+            n, k = workloads.SHAPES[name]
+            mat = head if name == "lm_head" else protos[name]
+            bufs[name] = (torch.randn((m, k), device="cuda").half(),
+                          torch.empty((m, n), dtype=torch.float16, device="cuda"),
+                          qt.new_workspace(mat.copies[0], m))
+        for layer in range(workloads.DECODE_LAYERS):
+            for name, _ in workloads.DECODE_LAYER_MATS:
+                x, y, ws = bufs[name]
+                c = protos[name].copies[layer]
+                launches.append(lambda x=x, c=c, y=y, ws=ws: qt.gemm(x, c, out=y, workspace=ws))
+                total += protos[name].bytes_for(m)
+        x, y, ws = bufs["lm_head"]
+        launches.append(lambda x=x, c=head.copies[0], y=y, ws=ws: qt.gemm(x, c, out=y, workspace=ws))
+        total += head.bytes_for(m)
+        g = capture(launches)
+        g.replay()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms_step = e0.elapsed_time(e1) / reps
+        out[m] = (ms_step, total / (ms_step * 1e-3) / 1e9, total)
+        log(f"decode step M={m}: {ms_step:.3f} ms, {out[m][1]:.0f} GB/s over {total / 1e9:.2f} GB "
+            f"({len(launches)} GEMMs)")
+        del g
+    del protos, head
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(rows):
@@ -276,6 +330,7 @@ def main():
     ws_g = qt.new_workspace(gate_up.copies[0], m)
     ws_d = qt.new_workspace(down.copies[0], m)
     step_bytes = gate_up.bytes_for(m) + down.bytes_for(m)
+    gate_up_bytes = gate_up.bytes_for(m)
 
     def step(i):
         qt.gemm(x1, gate_up.copies[i % r_steps], out=h, workspace=ws_g)
@@ -345,6 +400,12 @@ def main():
                            "frac_of_measured_ceiling": round(gbps / ceiling, 4)}
             log(f"{key}: {us:.1f} us {gbps:.0f} GB/s ({100 * gbps / ceiling:.1f}% of ceiling)")
 
+    decode = None
+    if args.all:
+        decode = {str(m): {"ms_per_step": round(v[0], 4), "GBps": round(v[1], 1),
+                           "weight_and_io_bytes": v[2], "frac_of_measured_ceiling": round(v[1] / ceiling, 4)}
+                  for m, v in decode_step().items()}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -374,12 +435,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "kernel": "gemm_kernel<NVFP4> on gate_up 34816x5120, M=1",
-                     "launch_us": round(gate_up_us, 3), "algorithmic_bytes": gate_up.bytes_for(m)},
+                     "launch_us": round(gate_up_us, 3), "algorithmic_bytes": gate_up_bytes},
         "measured_read_ceiling_GBps": round(ceiling, 1),
         "read_ceiling_at_gate_up_size_GBps": round(same_size, 1),
         "frac_of_measured_ceiling": round(value / ceiling, 4),
         "cpu_baseline": cpu,
         "per_matrix": extras,
+        "decode_step_27b": decode,
         "git": sha,
     }
     print(json.dumps(out), flush=True)

@@ -167,21 +167,38 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
                     void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
- * qpn_gemm with an explicit launch shape, for tuning sweeps. 0 in any field
- * means "choose automatically":
- *   split_k          cut K into this many ranges;
- *   waves_per_group  4 or 8 wavefronts (n-tiles) per workgroup;
+ * An explicit launch shape for qpn_gemm_tuned (tuning sweeps). 0 in any
+ * field means "choose automatically".
+ *   split_k          cut K into this many ranges over workgroups (their fp32
+ *                    partials are added by the last workgroup to finish);
+ *   waves_per_group  4 or 8 wavefronts per workgroup;
  *   depth            2, 3, 4, 6 or 8 units of the weight stream in flight per
- *                    wavefront.
- * A shape whose activation stage does not fit in LDS returns
- * QPN_ERR_UNSUPPORTED. The workspace an explicit split needs is
- * qpn_workspace_bytes_split(w, m, split_k) (0 also when the split is not
- * possible).
+ *                    wavefront;
+ *   k_slices         1, 2, 4 or 8 (at most waves_per_group): wavefronts of
+ *                    one workgroup that split one n-tile's K range and add
+ *                    their results through LDS.
  */
+typedef struct {
+  int32_t split_k;
+  int32_t waves_per_group;
+  int32_t depth;
+  int32_t k_slices;
+  int32_t reserved[4]; /* must be 0 */
+} qpn_launch;
+
+/* qpn_gemm with an explicit launch shape (NULL = automatic). A shape whose
+ * activation stage does not fit in LDS returns QPN_ERR_UNSUPPORTED. */
 qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
                           void* workspace_dev, size_t workspace_bytes,
-                          int32_t split_k, int32_t waves_per_group, int32_t depth, void* stream);
-size_t qpn_workspace_bytes_split(const qpn_weight* w, int32_t m, int32_t split_k);
+                          const qpn_launch* launch, void* stream);
+/* Workspace for qpn_gemm_tuned with this launch shape (0 if none is needed
+ * or the shape is not possible). */
+size_t qpn_workspace_bytes_tuned(const qpn_weight* w, int32_t m, const qpn_launch* launch);
+
+/* The launch shape qpn_gemm_tuned(w, m, launch) would use, every field
+ * resolved (launch NULL = what qpn_gemm uses): written to *resolved. Returns
+ * QPN_ERR_UNSUPPORTED for a shape that is not possible; no device work. */
+qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launch, qpn_launch* resolved);
 
 /*
  * Read-only streaming kernel that measures the HBM read ceiling the GEMM is

@@ -35,6 +35,16 @@ class QpnError(RuntimeError):
         super().__init__(f"{where}: {qpn_status_string(status)} ({status})")
 
 
+class qpn_launch(ctypes.Structure):
+    _fields_ = [
+        ("split_k", ctypes.c_int32),
+        ("waves_per_group", ctypes.c_int32),
+        ("depth", ctypes.c_int32),
+        ("k_slices", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
+    ]
+
+
 class qpn_weight(ctypes.Structure):
     _fields_ = [
         ("format", ctypes.c_int32),
@@ -53,6 +63,7 @@ _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 _F = ctypes.c_float
 _W = ctypes.POINTER(qpn_weight)
+_L = ctypes.POINTER(qpn_launch)
 
 # name -> (restype, argtypes); the declarations of include/qpn.h
 SIGNATURES = {
@@ -67,9 +78,10 @@ SIGNATURES = {
     "qpn_quantize_nvfp4": (_I32, [_P, _I64, _I64, _F, _P, _P, _P]),
     "qpn_quantize_fp8": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "qpn_workspace_bytes": (_SZ, [_W, _I32]),
-    "qpn_workspace_bytes_split": (_SZ, [_W, _I32, _I32]),
+    "qpn_workspace_bytes_tuned": (_SZ, [_W, _I32, _L]),
+    "qpn_gemm_plan": (_I32, [_W, _I32, _L, _L]),
     "qpn_gemm": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
-    "qpn_gemm_tuned": (_I32, [_P, _W, _P, _I32, _P, _SZ, _I32, _I32, _I32, _P]),
+    "qpn_gemm_tuned": (_I32, [_P, _W, _P, _I32, _P, _SZ, _L, _P]),
     "qpn_read_ceiling": (_I32, [_P, _SZ, _P, _I32, _P]),
     "qpn_read_ceiling_grid": (_I32, []),
 }
@@ -150,17 +162,31 @@ def qpn_workspace_bytes(weight, m):
     return lib().qpn_workspace_bytes(ctypes.byref(weight), m)
 
 
-def qpn_workspace_bytes_split(weight, m, split_k):
-    return lib().qpn_workspace_bytes_split(ctypes.byref(weight), m, split_k)
+def make_launch(split_k=0, waves_per_group=0, depth=0, k_slices=0):
+    return qpn_launch(split_k, waves_per_group, depth, k_slices)
+
+
+def qpn_workspace_bytes_tuned(weight, m, launch):
+    return lib().qpn_workspace_bytes_tuned(ctypes.byref(weight), m,
+                                           ctypes.byref(launch) if launch is not None else None)
+
+
+def qpn_gemm_plan(weight, m, launch=None):
+    """The resolved launch shape (a qpn_launch) qpn_gemm_tuned would use."""
+    out = qpn_launch()
+    _check(lib().qpn_gemm_plan(ctypes.byref(weight), m, ctypes.byref(launch) if launch is not None else None,
+                               ctypes.byref(out)), "qpn_gemm_plan")
+    return out
 
 
 def qpn_gemm(x, weight, y, m, workspace, workspace_bytes, stream):
     return _check(lib().qpn_gemm(x, ctypes.byref(weight), y, m, workspace, workspace_bytes, stream), "qpn_gemm")
 
 
-def qpn_gemm_tuned(x, weight, y, m, workspace, workspace_bytes, split_k, waves_per_group, depth, stream):
-    return _check(lib().qpn_gemm_tuned(x, ctypes.byref(weight), y, m, workspace, workspace_bytes, split_k,
-                                       waves_per_group, depth, stream), "qpn_gemm_tuned")
+def qpn_gemm_tuned(x, weight, y, m, workspace, workspace_bytes, launch, stream):
+    return _check(lib().qpn_gemm_tuned(x, ctypes.byref(weight), y, m, workspace, workspace_bytes,
+                                       ctypes.byref(launch) if launch is not None else None, stream),
+                  "qpn_gemm_tuned")
 
 
 def qpn_read_ceiling(buf, nbytes, sink, grid, stream):

@@ -132,24 +132,62 @@ qpn_status qpn_quantize_fp8(const float* w_dev, int64_t n, int64_t k, uint8_t* c
   return from_hip(qpn::launch_quantize_fp8(w_dev, n, k, codes_dev, row_scales_dev, as_stream(stream)));
 }
 
-size_t qpn_workspace_bytes_split(const qpn_weight* w, int32_t m, int32_t split_k) {
-  if (check_weight(w) != QPN_OK || m < 0 || m > QPN_MAX_M || split_k < 0) return 0;
+namespace {
+
+bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
+  if (!l) return true;
+  for (int i = 0; i < 4; ++i)
+    if (l->reserved[i] != 0) return false;
+  if (l->split_k < 0 || l->waves_per_group < 0 || l->depth < 0 || l->k_slices < 0) return false;
+  o->split = l->split_k;
+  o->waves = l->waves_per_group;
+  o->depth = l->depth;
+  o->k_slices = l->k_slices;
+  return true;
+}
+
+}  // namespace
+
+size_t qpn_workspace_bytes_tuned(const qpn_weight* w, int32_t m, const qpn_launch* launch) {
+  if (check_weight(w) != QPN_OK || m < 0 || m > QPN_MAX_M) return 0;
   if (m == 0 || w->n == 0) return 0;
+  qpn::LaunchOverride o;
+  if (!to_override(launch, &o)) return 0;
   qpn::GemmPlan p;
-  if (!qpn::plan_gemm(w->format, w->n, w->k, m, split_k, 0, 0, &p)) return 0;
+  if (!qpn::plan_gemm(w->format, w->n, w->k, m, o, &p)) return 0;
   return p.workspace_bytes;
 }
 
-size_t qpn_workspace_bytes(const qpn_weight* w, int32_t m) { return qpn_workspace_bytes_split(w, m, 0); }
+size_t qpn_workspace_bytes(const qpn_weight* w, int32_t m) { return qpn_workspace_bytes_tuned(w, m, nullptr); }
 
-qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
-                          void* workspace_dev, size_t workspace_bytes, int32_t split_k,
-                          int32_t waves_per_group, int32_t depth, void* stream) {
+qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launch, qpn_launch* resolved) {
   const qpn_status st = check_weight(w);
   if (st != QPN_OK) return st;
-  if (m < 0 || m > QPN_MAX_M || split_k < 0) return QPN_ERR_INVALID_ARG;
-  if (waves_per_group != 0 && waves_per_group != 4 && waves_per_group != 8) return QPN_ERR_INVALID_ARG;
-  if (depth != 0 && depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8)
+  if (!resolved || m < 1 || m > QPN_MAX_M || w->n == 0) return QPN_ERR_INVALID_ARG;
+  qpn::LaunchOverride o;
+  if (!to_override(launch, &o)) return QPN_ERR_INVALID_ARG;
+  qpn::GemmPlan p;
+  if (!qpn::plan_gemm(w->format, w->n, w->k, m, o, &p)) return QPN_ERR_UNSUPPORTED;
+  *resolved = qpn_launch{};
+  resolved->split_k = p.split;
+  resolved->waves_per_group = p.waves;
+  resolved->depth = p.depth;
+  resolved->k_slices = p.k_slices;
+  return QPN_OK;
+}
+
+qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
+                          void* workspace_dev, size_t workspace_bytes, const qpn_launch* launch,
+                          void* stream) {
+  const qpn_status st = check_weight(w);
+  if (st != QPN_OK) return st;
+  if (m < 0 || m > QPN_MAX_M) return QPN_ERR_INVALID_ARG;
+  qpn::LaunchOverride o;
+  if (!to_override(launch, &o)) return QPN_ERR_INVALID_ARG;
+  if (o.waves != 0 && o.waves != 4 && o.waves != 8) return QPN_ERR_INVALID_ARG;
+  if (o.depth != 0 && o.depth != 2 && o.depth != 3 && o.depth != 4 && o.depth != 6 && o.depth != 8)
+    return QPN_ERR_INVALID_ARG;
+  if (o.k_slices != 0 && o.k_slices != 1 && o.k_slices != 2 && o.k_slices != 4 && o.k_slices != 8)
     return QPN_ERR_INVALID_ARG;
   if (m == 0 || w->n == 0) return QPN_OK;
   if (!y_dev || !aligned(y_dev, 2)) return QPN_ERR_INVALID_ARG;
@@ -161,8 +199,7 @@ qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, i
   if (w->format == QPN_FMT_FP8_E4M3 && (!w->row_scales || !aligned(w->row_scales, 4)))
     return QPN_ERR_INVALID_ARG;
   qpn::GemmPlan p;
-  if (!qpn::plan_gemm(w->format, w->n, w->k, m, split_k, waves_per_group, depth, &p))
-    return QPN_ERR_UNSUPPORTED;
+  if (!qpn::plan_gemm(w->format, w->n, w->k, m, o, &p)) return QPN_ERR_UNSUPPORTED;
   if (p.workspace_bytes) {
     if (!workspace_dev || !aligned(workspace_dev, 16)) return QPN_ERR_INVALID_ARG;
     if (workspace_bytes < p.workspace_bytes) return QPN_ERR_BUFFER_TOO_SMALL;
@@ -173,7 +210,7 @@ qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, i
 
 qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
                     void* workspace_dev, size_t workspace_bytes, void* stream) {
-  return qpn_gemm_tuned(x_dev, w, y_dev, m, workspace_dev, workspace_bytes, 0, 0, 0, stream);
+  return qpn_gemm_tuned(x_dev, w, y_dev, m, workspace_dev, workspace_bytes, nullptr, stream);
 }
 
 int32_t qpn_read_ceiling_grid(void) { return qpn::read_ceiling_default_grid(); }

@@ -28,14 +28,59 @@
 namespace qpn {
 namespace {
 
-constexpr size_t kLdsBudget = 64 * 1024;
-// Launch-shape heuristic, from a sweep of split x waves x depth on MI355X
-// over the 27B shapes (N-tiles 320..9496, K units 20..68, M 1..8): the best
-// split puts about 960 wavefronts (n-tiles x K ranges) on the chip, a
-// stream depth of 3 units is within noise of the best everywhere, and
-// 8-wave workgroups only pay off on very wide matrices.
-constexpr int kTargetWaves = 960;
-constexpr int kWideTiles = 4096;
+// Activation stage per workgroup: two workgroups of up to this size (plus a
+// few bytes of static LDS) fit the 160 KiB of LDS in a CU.
+constexpr size_t kLdsBudget = 79 * 1024;
+// Launch shapes. For the matrices of a ~27B dense decoder (hidden 5120) the
+// launch comes from a table measured on MI355X: a sweep of workgroup size x
+// K slices x K split x stream depth, best graph-replayed time per launch at
+// M = 1, 2, 4, 8. Other shapes use a rule distilled from the same sweep:
+//  * a workgroup holds TN n-tiles that share one staged copy of x (the
+//    staging reads 2*M bytes of x per K element against 9*TN bytes of NVFP4
+//    weights), TN = 2 up to M = 4 and 4 above;
+//  * the rest of an 8-wavefront workgroup splits each n-tile's K range into
+//    K slices, reduced through LDS, keeping >= kMinSliceUnits units a slice;
+//  * K is split over workgroups only as far as the activation stage must be
+//    cut to fit LDS (that reduction costs memory round trips at the tail);
+//  * a stream depth of 3 units.
+struct TunedLaunch {
+  int fmt;
+  int64_t n, k;
+  int m_max;  // entry applies to m <= m_max (entries of a shape in increasing m_max)
+  int waves, k_slices, split, depth;
+};
+
+constexpr TunedLaunch kTuned[] = {
+    // NVFP4 gate_up 34816 x 5120
+    {kFmtNvfp4, 34816, 5120, 1, 4, 4, 1, 3}, {kFmtNvfp4, 34816, 5120, 2, 4, 4, 1, 2},
+    {kFmtNvfp4, 34816, 5120, 4, 8, 4, 1, 2}, {kFmtNvfp4, 34816, 5120, 8, 8, 2, 2, 2},
+    // NVFP4 down 5120 x 17408
+    {kFmtNvfp4, 5120, 17408, 2, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 17408, 4, 8, 2, 3, 2},
+    {kFmtNvfp4, 5120, 17408, 8, 8, 2, 6, 2},
+    // NVFP4 qkv 7168 x 5120 and o_proj 5120 x 5120
+    {kFmtNvfp4, 7168, 5120, 4, 8, 4, 1, 3}, {kFmtNvfp4, 7168, 5120, 8, 8, 2, 2, 2},
+    {kFmtNvfp4, 5120, 5120, 4, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 5120, 8, 8, 2, 3, 2},
+    // NVFP4 lm_head 151936 x 5120
+    {kFmtNvfp4, 151936, 5120, 1, 8, 4, 1, 3}, {kFmtNvfp4, 151936, 5120, 2, 4, 2, 1, 2},
+    {kFmtNvfp4, 151936, 5120, 4, 8, 2, 1, 2}, {kFmtNvfp4, 151936, 5120, 8, 8, 1, 2, 2},
+    // FP8 qkv 7168 x 5120
+    {kFmtFp8, 7168, 5120, 4, 4, 2, 1, 2}, {kFmtFp8, 7168, 5120, 8, 8, 2, 2, 2},
+    // FP8 o_proj 5120 x 5120
+    {kFmtFp8, 5120, 5120, 2, 4, 2, 1, 3}, {kFmtFp8, 5120, 5120, 4, 8, 4, 1, 2},
+    {kFmtFp8, 5120, 5120, 8, 8, 2, 3, 2},
+    // FP8 down 5120 x 17408
+    {kFmtFp8, 5120, 17408, 2, 8, 4, 1, 2}, {kFmtFp8, 5120, 17408, 4, 8, 2, 3, 3},
+    {kFmtFp8, 5120, 17408, 8, 8, 2, 6, 2},
+};
+
+const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
+  for (const TunedLaunch& t : kTuned)
+    if (t.fmt == fmt && t.n == n && t.k == k && m <= t.m_max) return &t;
+  return nullptr;
+}
+
+constexpr int kMinSliceUnits = 4;
+
 constexpr int kRowPad = 8;          // fp16 pad per staged row (bank spread)
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -57,7 +102,10 @@ __device__ __forceinline__ void lds_dma16(const void* src, _Float16* lds_dst) {
 
 __device__ __forceinline__ h8 x_fragment(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
 
-__device__ __forceinline__ void unit_mfma(const Unit<kFmtNvfp4>& w, const _Float16* xrow, f4& acc) {
+// The eight MFMA steps of a unit alternate between two accumulators, which
+// halves the chain of dependent matrix instructions per wavefront; the two
+// are added once at the end (a fixed order, so results stay reproducible).
+__device__ __forceinline__ void unit_mfma(const Unit<kFmtNvfp4>& w, const _Float16* xrow, f4 (&acc)[2]) {
   const h2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.sc, 1.0f, false);
   const h2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.sc, 1.0f, true);
   const h2 sc[4] = {h2{s01.x, s01.x}, h2{s01.y, s01.y}, h2{s23.x, s23.x}, h2{s23.y, s23.y}};
@@ -66,18 +114,18 @@ __device__ __forceinline__ void unit_mfma(const Unit<kFmtNvfp4>& w, const _Float
     const uint32_t d = word(t < 4 ? w.c0 : w.c1, t & 3);
     const h8 a = decode_fp4x8(d, sc[t >> 1]);
     const h8 b = x_fragment(xrow + t * 8);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    acc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t & 1], 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void unit_mfma(const Unit<kFmtFp8>& w, const _Float16* xrow, f4& acc) {
+__device__ __forceinline__ void unit_mfma(const Unit<kFmtFp8>& w, const _Float16* xrow, f4 (&acc)[2]) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const u4& v = w.q[t >> 1];
     const int i = (t & 1) * 2;
     const h8 a = decode_fp8x8(word(v, i), word(v, i + 1));
     const h8 b = x_fragment(xrow + t * 8);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    acc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t & 1], 0, 0, 0);
   }
 }
 
@@ -86,7 +134,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     const _Float16* __restrict__ x, const uint8_t* packed,
     const float* __restrict__ row_scales, float tensor_scale, _Float16* __restrict__ y,
     float* __restrict__ ws, int* __restrict__ counters, int M, int N, int K, int NT, int KU, int ups,
-    int stride) {
+    int stride, int KS) {
   extern __shared__ __align__(16) _Float16 xs[];
   __shared__ int last_group;
   constexpr int kBytes = Unit<FMT>::kBytes;
@@ -97,11 +145,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   const int s = blockIdx.y;
   const int u0 = s * ups;
   const int nu = min(KU - u0, ups);
-  const int nt = blockIdx.x * WAVES + wave;
+  // The workgroup's WAVES wavefronts cover TN n-tiles x KS slices of its K
+  // range: wavefront (tn, ks) streams n-tile tn over the ks-th slice.
+  const int TN = WAVES / KS;
+  const int tn = wave % TN;
+  const int ks = wave / TN;
+  const int sub = (nu + KS - 1) / KS;
+  const int wu0 = min(ks * sub, nu);
+  const int wnu = min(sub, nu - wu0);
+  const int nt = blockIdx.x * TN + tn;
   const bool active = nt < NT;
   const uint32_t unit_stride = static_cast<uint32_t>(NT) * kBytes;
-  const Stream stream(packed + unit_offset(active ? nt : 0, u0, NT, kBytes),
-                      active && nu > 0 ? static_cast<uint32_t>(nu - 1) * unit_stride + kBytes : 0u,
+  const Stream stream(packed + unit_offset(active ? nt : 0, u0 + wu0, NT, kBytes),
+                      active && wnu > 0 ? static_cast<uint32_t>(wnu - 1) * unit_stride + kBytes : 0u,
                       unit_stride);
 
   // Stage this K range of every activation row in LDS with direct-to-LDS
@@ -158,18 +214,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   // stored, and MFMA output columns do not mix, so they need no zeroing.
   const int mcol = lane & 15;
   const int g = lane >> 4;
-  const _Float16* xrow = xs + min(mcol, M - 1) * stride + g * 64;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  const _Float16* xrow = xs + min(mcol, M - 1) * stride + g * 64 + wu0 * kUnitK;
+  f4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 
   if (active) {
     // Each slot of buf is consumed and then refilled in place (unit u + DEPTH
     // goes where unit u was), so the loop carries no register copies and
     // keeps DEPTH-1 units in flight while it computes. Refills past the end
     // of the range read zeros and cost no memory traffic.
-    for (int base = 0; base < nu; base += DEPTH) {
+    for (int base = 0; base < wnu; base += DEPTH) {
 #pragma unroll
       for (int i = 0; i < DEPTH; ++i) {
-        if (base + i < nu) unit_mfma(buf[i], xrow + (base + i) * kUnitK, acc);
+        if (base + i < wnu) unit_mfma(buf[i], xrow + (base + i) * kUnitK, acc2);
         load_unit(buf[i], stream, base + DEPTH + i, lane);
         // keep the scheduler from sinking the refill below the next units' math
         __builtin_amdgcn_sched_barrier(0);
@@ -177,10 +233,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     }
   }
 
+  f4 acc = acc2[0] + acc2[1];
+
+  // The KS slices of each n-tile are added through LDS, in slice order, into
+  // the slice-0 wavefront. The staged activations are dead by now, so their
+  // LDS (sized for this by the launcher) holds the partial tiles.
+  if (KS > 1) {
+    f4* red = reinterpret_cast<f4*>(xs);
+    __syncthreads();
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (ks == 0) {
+      for (int j = 1; j < KS; ++j) acc += red[(j * TN + tn) * 64 + lane];
+    }
+  }
+  const bool owner = active && ks == 0;
+
   // Lane (m = lane % 16, g = lane / 16) holds rows n = 4g + r of column m.
   const int n0 = nt * kTileN + g * 4;
   if (S == 1) {
-    if (active && mcol < M) {
+    if (owner && mcol < M) {
       _Float16* dst = y + static_cast<size_t>(mcol) * N;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -207,7 +279,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   // thread waits for its partial stores to be acknowledged before the
   // workgroup barrier that precedes the counter increment, and the last
   // workgroup issues its loads only after the increment has returned.
-  if (active && mcol < M) {
+  if (owner && mcol < M) {
     float* dst = ws + (static_cast<size_t>(s) * M + mcol) * N;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -220,7 +292,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
                  S - 1;
   __syncthreads();
   if (!last_group) return;
-  const int rows = WAVES * kTileN;
+  const int rows = TN * kTileN;
   const int nbase = blockIdx.x * rows;
   for (int idx = tid; idx < M * rows; idx += WAVES * 64) {
     const int m = idx / rows;
@@ -242,7 +314,12 @@ hipError_t launch_cfg(const GemmPlan& p, const void* x, const void* packed, cons
                       hipStream_t stream) {
   const int NT = static_cast<int>(ceil_div(n, kTileN));
   const int KU = static_cast<int>(ceil_div(k, kUnitK));
-  const unsigned groups = static_cast<unsigned>(ceil_div(NT, WAVES));
+  const unsigned groups = static_cast<unsigned>(ceil_div(NT, WAVES / p.k_slices));
+  // Dynamic LDS above the 64 KiB default must be allowed per kernel.
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBudget));
+  if (attr != hipSuccess) return attr;
   int* counters = p.split > 1 ? static_cast<int*>(workspace) : nullptr;
   float* ws = p.split > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.partials_offset)
                           : nullptr;
@@ -250,7 +327,7 @@ hipError_t launch_cfg(const GemmPlan& p, const void* x, const void* packed, cons
                      dim3(WAVES * 64), p.lds_bytes, stream, static_cast<const _Float16*>(x),
                      static_cast<const uint8_t*>(packed), row_scales, tensor_scale,
                      static_cast<_Float16*>(y), ws, counters, m, static_cast<int>(n),
-                     static_cast<int>(k), NT, KU, p.units_per_split, p.lds_stride);
+                     static_cast<int>(k), NT, KU, p.units_per_split, p.lds_stride, p.k_slices);
   return hipGetLastError();
 }
 
@@ -269,44 +346,69 @@ hipError_t launch_depth(const GemmPlan& p, const void* x, const void* packed, co
 
 }  // namespace
 
-bool plan_gemm(int fmt, int64_t n, int64_t k, int m, int split_override, int waves_override,
-               int depth_override, GemmPlan* p) {
+bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, GemmPlan* p) {
   if (fmt != kFmtNvfp4 && fmt != kFmtFp8) return false;
   if (m < 1 || m > kMaxM || n < 1 || k < 0) return false;
   const int64_t NT = ceil_div(n, kTileN);
-  const int waves = waves_override ? waves_override : (NT >= kWideTiles ? 8 : 4);
-  if (waves != 4 && waves != 8) return false;
-  const int depth = depth_override ? depth_override : 3;
-  if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
   const int64_t KU = ceil_div(k, kUnitK);
   const int64_t unit_bytes = fmt == kFmtNvfp4 ? kNvUnitBytes : kF8UnitBytes;
   // unit offsets inside one wavefront's stream are 32-bit
   if (NT * KU * unit_bytes >= (int64_t(1) << 31)) return false;
   const int64_t max_ups = (static_cast<int64_t>(kLdsBudget) / (2 * m) - kRowPad) / kUnitK;
-  int64_t split;
-  if (split_override > 0) {
-    split = split_override;
-  } else {
-    const int64_t s_lds = KU ? ceil_div(KU, max_ups) : 1;
-    const int64_t s_occ = (kTargetWaves + NT / 2) / NT;  // nearest
-    split = s_lds > s_occ ? s_lds : s_occ;
+  if (max_ups < 1) return false;
+
+  // A tuned launch for this shape fills in what the caller left automatic.
+  LaunchOverride w = o;
+  if (const TunedLaunch* t = find_tuned(fmt, n, k, m)) {
+    if (!w.split) w.split = t->split;
+    if (!w.waves) w.waves = t->waves;
+    if (!w.k_slices) w.k_slices = t->k_slices;
+    if (!w.depth) w.depth = t->depth;
   }
+
+  // K ranges over workgroups: as few as the LDS stage allows.
+  int64_t split = w.split > 0 ? w.split : (KU ? ceil_div(KU, max_ups) : 1);
   if (split > KU) split = KU ? KU : 1;
   if (split < 1) split = 1;
-  int64_t ups = KU ? ceil_div(KU, split) : 0;
+  const int64_t ups = KU ? ceil_div(KU, split) : 0;
   if (KU) split = ceil_div(KU, ups);
   if (ups > max_ups) return false;
+
+  // n-tiles per workgroup first (from M), then as many K slices per n-tile
+  // as the workgroup has room for and the K range supports.
+  const int tn_target = m > 4 ? 4 : 2;
+  int ks = w.k_slices;
+  if (!ks) {
+    const int ks_room = 8 / tn_target;
+    ks = 1;
+    while (ks < ks_room && ceil_div(ups, 2 * ks) >= kMinSliceUnits) ks *= 2;
+  }
+  int waves = w.waves;
+  if (!waves) {
+    waves = tn_target * ks < 4 ? 4 : tn_target * ks > 8 ? 8 : tn_target * ks;
+    if (waves < ks) waves = ks;
+  }
+  if (waves != 4 && waves != 8) return false;
+  if (ks != 1 && ks != 2 && ks != 4 && ks != 8) return false;
+  if (ks > waves) return false;
+  const int depth = w.depth ? w.depth : 3;
+  if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
+
   p->split = static_cast<int>(split);
   p->waves = waves;
   p->depth = depth;
+  p->k_slices = ks;
   p->units_per_split = static_cast<int>(ups);
   p->lds_stride = static_cast<int>(ups * kUnitK + kRowPad);
   p->lds_bytes = static_cast<size_t>(m) * p->lds_stride * sizeof(_Float16);
+  // K slices reduce through the same LDS: one 16x16 fp32 tile per wavefront.
+  const size_t red_bytes = ks > 1 ? static_cast<size_t>(waves) * 64 * sizeof(f4) : 0;
+  if (p->lds_bytes < red_bytes) p->lds_bytes = red_bytes;
   if (split > 1) {
-    // Counters first, sized for the smallest workgroup (4 n-tiles), so that
-    // their place does not depend on m, split or workgroup size and a
-    // workspace can be shared by calls with different row counts.
-    const size_t counters = static_cast<size_t>(ceil_div(NT, 4)) * sizeof(int);
+    // Counters first, one per n-tile (enough for any grouping of n-tiles),
+    // so that their place does not depend on m, split or workgroup shape and
+    // a workspace can be shared by calls with different row counts.
+    const size_t counters = static_cast<size_t>(NT) * sizeof(int);
     p->partials_offset = (counters + 255) & ~size_t(255);
     p->workspace_bytes = p->partials_offset + static_cast<size_t>(split) * m * n * sizeof(float);
   } else {

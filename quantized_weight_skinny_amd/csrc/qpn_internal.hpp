@@ -12,9 +12,14 @@ namespace qpn {
 // handles `waves` n-tiles of one piece. split > 1 writes fp32 partial sums to
 // the workspace; the last workgroup of a group to finish adds them in piece
 // order.
+struct LaunchOverride {
+  int split = 0, waves = 0, depth = 0, k_slices = 0;  // 0 = automatic
+};
+
 struct GemmPlan {
   int split;
   int waves;
+  int k_slices;    // wavefronts of a workgroup that split one n-tile's K range
   int depth;       // units of the weight stream each wavefront keeps in flight
   int units_per_split;
   int lds_stride;  // halves per staged activation row
@@ -23,8 +28,7 @@ struct GemmPlan {
   size_t workspace_bytes;  // fp32 partials [split][m][n] from this offset (0 if split == 1)
 };
 
-bool plan_gemm(int fmt, int64_t n, int64_t k, int m, int split_override, int waves_override,
-               int depth_override, GemmPlan* plan);
+bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, GemmPlan* plan);
 
 hipError_t launch_gemm(int fmt, const GemmPlan& plan, const void* x, const void* packed,
                        const float* row_scales, float tensor_scale, void* y, void* workspace,

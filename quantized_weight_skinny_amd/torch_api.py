@@ -27,7 +27,8 @@ from . import (
     qpn_unpack_fp8,
     qpn_unpack_nvfp4,
     qpn_workspace_bytes,
-    qpn_workspace_bytes_split,
+    qpn_workspace_bytes_tuned,
+    make_launch,
 )
 
 
@@ -148,18 +149,25 @@ def quantize_fp8(w):
     return codes, rs
 
 
-def workspace_bytes(pw, m, split_k=0):
+def _launch(split_k=0, waves=0, depth=0, k_slices=0):
+    if split_k or waves or depth or k_slices:
+        return make_launch(split_k, waves, depth, k_slices)
+    return None
+
+
+def workspace_bytes(pw, m, split_k=0, waves=0, depth=0, k_slices=0):
+    launch = _launch(split_k, waves, depth, k_slices)
     d = pw.desc()
-    return qpn_workspace_bytes_split(d, m, split_k) if split_k else qpn_workspace_bytes(d, m)
+    return qpn_workspace_bytes_tuned(d, m, launch) if launch is not None else qpn_workspace_bytes(d, m)
 
 
-def new_workspace(pw, m, split_k=0, device="cuda"):
+def new_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, device="cuda"):
     """A zeroed workspace for gemm(pw) with m rows (None when none is needed)."""
-    need = workspace_bytes(pw, m, split_k)
+    need = workspace_bytes(pw, m, split_k, waves, depth, k_slices)
     return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
 
 
-def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0):
+def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0):
     """y[m, n] = x[m, k] @ dequant(W)^T in fp16 through qpn_gemm.
 
     A workspace, when one is needed and not given, is allocated zeroed per
@@ -169,13 +177,14 @@ def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0):
     if out is None:
         out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
     d = pw.desc()
-    need = qpn_workspace_bytes_split(d, m, split_k) if split_k else qpn_workspace_bytes(d, m)
+    launch = _launch(split_k, waves, depth, k_slices)
+    need = qpn_workspace_bytes_tuned(d, m, launch) if launch is not None else qpn_workspace_bytes(d, m)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if need else 0
-    if split_k or waves or depth:
-        qpn_gemm_tuned(x.data_ptr(), d, out.data_ptr(), m, ws_ptr, ws_bytes, split_k, waves, depth, _stream())
+    if launch is not None:
+        qpn_gemm_tuned(x.data_ptr(), d, out.data_ptr(), m, ws_ptr, ws_bytes, launch, _stream())
     else:
         qpn_gemm(x.data_ptr(), d, out.data_ptr(), m, ws_ptr, ws_bytes, _stream())
     return out

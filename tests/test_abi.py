@@ -61,8 +61,14 @@ def _w(fmt=q.QPN_FMT_NVFP4, n=512, k=1024, packed=FAKE, rs=FAKE):
     return q.make_weight(fmt, n, k, packed, 1.0, rs)
 
 
-def _gemm(x, w, y, m, ws=None, wsb=0, split=0, waves=0, depth=0):
-    return q.lib().qpn_gemm_tuned(x, ctypes.byref(w), y, m, ws, wsb, split, waves, depth, None)
+def _gemm(x, w, y, m, ws=None, wsb=0, split=0, waves=0, depth=0, k_slices=0, reserved=0):
+    launch = q.make_launch(split, waves, depth, k_slices)
+    launch.reserved[0] = reserved
+    return q.lib().qpn_gemm_tuned(x, ctypes.byref(w), y, m, ws, wsb, ctypes.byref(launch), None)
+
+
+def _ws(w, m, split=0, waves=0, depth=0, k_slices=0):
+    return q.qpn_workspace_bytes_tuned(w, m, q.make_launch(split, waves, depth, k_slices))
 
 
 def test_gemm_rejects_bad_arguments_before_any_device_call():
@@ -79,6 +85,9 @@ def test_gemm_rejects_bad_arguments_before_any_device_call():
     assert _gemm(FAKE, _w(fmt=q.QPN_FMT_FP8_E4M3, rs=None), FAKE, 1) == err  # FP8 needs row scales
     assert _gemm(FAKE, _w(), FAKE, 1, waves=5) == err
     assert _gemm(FAKE, _w(), FAKE, 1, depth=5) == err
+    assert _gemm(FAKE, _w(), FAKE, 1, k_slices=3) == err
+    assert _gemm(FAKE, _w(), FAKE, 1, reserved=1) == err
+    assert _gemm(FAKE, _w(), FAKE, 1, waves=4, k_slices=8) == q.QPN_ERR_UNSUPPORTED
     w = _w()
     w.reserved = 1
     assert _gemm(FAKE, w, FAKE, 1) == err
@@ -97,16 +106,35 @@ def test_gemm_workspace_checks():
     assert need > 0                                           # small N splits K
     assert _gemm(FAKE, w, FAKE, 8, None, 0) == q.QPN_ERR_INVALID_ARG
     assert _gemm(FAKE, w, FAKE, 8, FAKE, need - 16) == q.QPN_ERR_BUFFER_TOO_SMALL
-    # one counter per group of 4 n-tiles (padded to 256 bytes), then fp32 partials [split][m][n]
-    counters = (5120 // 16 // 4) * 4
-    assert q.qpn_workspace_bytes_split(w, 8, 5) == (counters + 255) // 256 * 256 + 5 * 8 * 5120 * 4
+    # one counter per n-tile (padded to 256 bytes), then fp32 partials [split][m][n]
+    counters = (5120 // 16) * 4
+    assert _ws(w, 8, split=5) == (counters + 255) // 256 * 256 + 5 * 8 * 5120 * 4
     # one K range of 17408 x 8 rows does not fit the activation stage in LDS
-    assert q.qpn_workspace_bytes_split(w, 8, 1) == 0
+    assert _ws(w, 8, split=1) == 0
     assert _gemm(FAKE, w, FAKE, 8, FAKE, need, split=1) == q.QPN_ERR_UNSUPPORTED
-    assert q.qpn_workspace_bytes_split(_w(n=5120, k=4096), 1, 1) == 0
+    assert _ws(_w(n=5120, k=4096), 1, split=1) == 0
+    assert _ws(_w(n=5120, k=4096), 1, split=1, k_slices=4) == 0     # K slices need no workspace
     # gate_up at M=1 fills the chip without splitting K
     assert q.qpn_workspace_bytes(_w(n=34816, k=5120), 1) == 0
     assert q.qpn_workspace_bytes(_w(), 17) == 0
+
+
+def test_plan_resolves_tuned_and_rule_based_launches():
+    # the 27B gate_up at M=1 comes from the tuned table
+    p = q.qpn_gemm_plan(_w(n=34816, k=5120), 1)
+    assert (p.split_k, p.waves_per_group, p.k_slices, p.depth) == (1, 4, 4, 3)
+    # down at M=8 must split K: 17408 x 8 rows do not fit one LDS stage
+    p = q.qpn_gemm_plan(_w(n=5120, k=17408), 8)
+    assert p.split_k > 1 and p.k_slices >= 1
+    # any other shape goes through the rule: valid values, explicit fields kept
+    p = q.qpn_gemm_plan(_w(n=1000, k=3072), 3, q.make_launch(depth=6))
+    assert p.depth == 6 and p.waves_per_group in (4, 8) and p.k_slices in (1, 2, 4, 8)
+    assert p.waves_per_group % p.k_slices == 0 and p.split_k >= 1
+    for m in range(1, 17):
+        p = q.qpn_gemm_plan(_w(n=777, k=17408), m)
+        assert p.split_k * 65536 >= 0 and p.waves_per_group in (4, 8)
+    with pytest.raises(q.QpnError):
+        q.qpn_gemm_plan(_w(n=5120, k=17408), 8, q.make_launch(split_k=1))
 
 
 def test_pack_and_quantize_reject_bad_arguments():

@@ -37,13 +37,26 @@ def test_gemm_parity_small(fmt, m, n, k):
     _parity(fmt, m, n, k, seed=1000 + n + k + m)
 
 
+LAUNCHES = [(1, 4, 2, 1), (2, 4, 3, 1), (3, 8, 4, 1), (5, 4, 6, 1), (7, 8, 8, 1), (0, 8, 0, 0),
+            (4, 4, 8, 1), (1, 8, 6, 1), (1, 4, 3, 4), (1, 8, 3, 8), (2, 8, 4, 2), (3, 4, 2, 2),
+            (1, 8, 2, 4), (7, 8, 3, 8)]
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
-@pytest.mark.parametrize("split,waves,depth", [(1, 4, 2), (2, 4, 3), (3, 8, 4), (5, 4, 6), (7, 8, 8),
-                                               (0, 8, 0), (4, 4, 8), (1, 8, 6)])
-def test_gemm_launch_shapes_agree(fmt, split, waves, depth):
+@pytest.mark.parametrize("split,waves,depth,k_slices", LAUNCHES)
+def test_gemm_launch_shapes_agree(fmt, split, waves, depth, k_slices):
     n, k, m = 96, 1792, 5
-    say("gemm tuned", fmt, split, waves, depth)
-    _parity(fmt, m, n, k, seed=77, split_k=split, waves=waves, depth=depth)
+    say("gemm tuned", fmt, split, waves, depth, k_slices)
+    _parity(fmt, m, n, k, seed=77, split_k=split, waves=waves, depth=depth, k_slices=k_slices)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("k_slices", [2, 4, 8])
+def test_k_slices_ragged(fmt, k_slices):
+    """K slices that do not divide the K range evenly (and slices left empty)."""
+    say("k slices ragged", fmt, k_slices)
+    _parity(fmt, 3, 50, 1552, seed=88, waves=8, k_slices=k_slices)       # 7 units, ragged tail
+    _parity(fmt, 2, 33, 256, seed=89, waves=8, k_slices=k_slices)        # 1 unit: most slices empty
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
@@ -55,12 +68,13 @@ def test_split_k_workspace_reuse_is_deterministic(fmt):
     w = workloads.weights(n, k, 21)
     pw, _ = gpu_quantize(fmt, to_dev(w))
     ws = qt.new_workspace(pw, 16, split_k=6)
+    assert ws.numel() >= qt.workspace_bytes(pw, 8, split_k=6, k_slices=2)
     assert ws is not None
     outs = []
     for m in (8, 3, 8, 16, 8):
         x = to_dev(workloads.activations(m, k, 22)[:m])
         outs.append((m, to_host(qt.gemm(x, pw, workspace=ws, split_k=6))))
-    assert not to_host(ws[:(n // 16 // 4) * 4]).any()  # counters back at zero
+    assert not to_host(ws[:(n // 16) * 4]).any()  # counters back at zero
     ref8 = outs[0][1]
     for m, y in outs:
         if m == 8:
@@ -184,10 +198,12 @@ def test_empty_and_degenerate_shapes():
 
 
 FULL = [
-    ("nvfp4", "gate_up", 1), ("nvfp4", "down", 1),
+    ("nvfp4", "gate_up", 1), ("nvfp4", "down", 1), ("nvfp4", "gate_up", 2), ("nvfp4", "down", 4),
     ("nvfp4", "gate_up", 8), ("nvfp4", "down", 8), ("nvfp4", "qkv", 8), ("nvfp4", "o_proj", 8),
-    ("fp8", "qkv", 1), ("fp8", "qkv", 4), ("fp8", "down", 2), ("fp8", "down", 4),
-    ("nvfp4", "lm_head", 8),
+    ("nvfp4", "qkv", 1), ("nvfp4", "o_proj", 3),
+    ("fp8", "qkv", 1), ("fp8", "qkv", 4), ("fp8", "qkv", 8), ("fp8", "down", 2), ("fp8", "down", 4),
+    ("fp8", "down", 7), ("fp8", "o_proj", 1), ("fp8", "o_proj", 4), ("fp8", "o_proj", 8),
+    ("nvfp4", "lm_head", 1), ("nvfp4", "lm_head", 8),
 ]
 
 
@@ -197,7 +213,7 @@ def test_full_size_sampled_outputs(fmt, matrix, m):
     oracle recomputes a sample of output columns (every row of x)."""
     n, k = workloads.SHAPES[matrix]
     say("full size", fmt, matrix, m, n, k)
-    wl = "nvfp4_27b_m8" if fmt == "nvfp4" else "fp8_27b_m124"
+    wl = "decode_step_27b"
     w = workloads.weights(n, k, workloads.seed_for(wl, matrix, "W"))
     x = workloads.activations(m, k, workloads.seed_for(wl, matrix, "x"))
     wd = to_dev(w)
