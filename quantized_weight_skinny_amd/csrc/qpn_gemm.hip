@@ -80,6 +80,7 @@ const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
 }
 
 constexpr int kMinSliceUnits = 4;
+constexpr int kFixupBatch = 8;  // split-K partials loaded together by the last workgroup
 
 constexpr int kRowPad = 8;          // fp16 pad per staged row (bank spread)
 
@@ -299,9 +300,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     const int n = nbase + (idx - m * rows);
     if (n >= N) continue;
     const float* src = ws + static_cast<size_t>(m) * N + n;
+    const size_t range_stride = static_cast<size_t>(M) * N;
+    // The ranges' partials are fetched kFixupBatch at a time, all loads of a
+    // batch in flight together (one memory round trip per batch, not per
+    // range), and added in range order.
     float sum = 0.f;
-    for (int r = 0; r < S; ++r)
-      sum += __hip_atomic_load(src + static_cast<size_t>(r) * M * N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int r0 = 0; r0 < S; r0 += kFixupBatch) {
+      float part[kFixupBatch];
+#pragma unroll
+      for (int j = 0; j < kFixupBatch; ++j)
+        part[j] = r0 + j < S ? __hip_atomic_load(src + (r0 + j) * range_stride, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : 0.f;
+#pragma unroll
+      for (int j = 0; j < kFixupBatch; ++j)
+        if (r0 + j < S) sum += part[j];
+    }
     const float scale = FMT == kFmtNvfp4 ? tensor_scale : row_scales[n];
     y[static_cast<size_t>(m) * N + n] = static_cast<_Float16>(sum * scale);
   }
