@@ -9,9 +9,12 @@ enough distinct copies (>= 2 GiB) that no launch finds its matrix in the
 Prints one JSON line. ``value`` is the effective HBM read bandwidth of the
 step (algorithmic bytes: packed codes + block scales + x + y, divided by the
 step time). Also reported: the read-only streaming ceiling measured in the
-same run, per-matrix times for M=1 and M=8 (and FP8 M=1,2,4 and the full
-64-layer decode step with --all), the roofline of the dominant kernel, and
-the CPU oracle timed on a bounded sample (baseline only).
+same run (on a 4 GiB buffer and at the size of each large matrix), per-matrix
+times for every workload (NVFP4 M=1 and M=8, FP8 M=1,2,4, the GEMV case, the
+per-GPU shapes of 4-way tensor parallelism, the 16-row verify block), the
+full 64-layer decode step as stream-ordered launches and as one HIP graph,
+the roofline of the dominant kernel, and the CPU oracle timed on a bounded
+sample (baseline only). ``--quick`` keeps only the headline step.
 """
 
 import argparse
@@ -31,10 +34,38 @@ import workloads  # noqa: E402
 METRIC = "effective HBM read GB/s (% of ceiling), NVFP4/FP8 skinny GEMM at M=1 and M=8"
 PEAK_HBM_GBPS = 8000.0
 ROTATE_BYTES = 2.5e9
+MAX_COPIES = 256  # the GEMV case stays cache-resident even so (it is reported, not judged)
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class mark:
+    """A named ROCTx range around a measurement, so that a profiler run with
+    marker tracing can attribute each kernel dispatch to its workload; a
+    no-op when the ROCTx library is not there."""
+    _lib = None
+
+    def __init__(self, name):
+        self.name = name.encode()
+        if mark._lib is None:
+            import ctypes
+            mark._lib = False
+            for so in ("librocprofiler-sdk-roctx.so.1", "libroctx64.so.4"):
+                try:
+                    mark._lib = ctypes.CDLL(so)
+                    break
+                except OSError:
+                    continue
+
+    def __enter__(self):
+        if mark._lib:
+            mark._lib.roctxRangePushA(self.name)
+
+    def __exit__(self, *exc):
+        if mark._lib:
+            mark._lib.roctxRangePop()
 
 
 def parse():
@@ -42,9 +73,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--all", action="store_true", help="also FP8 M=1,2,4 and the 64-layer decode step")
+    p.add_argument("--quick", action="store_true", help="only the headline step (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-extras", action="store_true", help="only the headline step")
     p.add_argument("--cpu-rows", type=int, default=1024, help="rows per matrix in the CPU oracle sample")
     return p.parse_args()
 
@@ -71,7 +101,7 @@ class Mat:
             del codes
         del wd
         self.weight_bytes = pw.nbytes
-        r = copies or max(1, int(np.ceil(ROTATE_BYTES / self.weight_bytes)))
+        r = copies or min(MAX_COPIES, max(1, int(np.ceil(ROTATE_BYTES / self.weight_bytes))))
         self.copies = [pw]
         for _ in range(r - 1):
             rs = pw.row_scales.clone() if pw.row_scales is not None else None
@@ -96,9 +126,14 @@ def capture(launches):
     return g
 
 
-def time_matrix(mat, m, reps=3):
+def time_matrix(mat, m, reps=3, label=None):
     """Average µs per launch of one matrix: a graph of back-to-back launches
     over all rotating copies, timed with events on the launch stream."""
+    with mark(label or f"{mat.fmt}_m{m}/{mat.name}"):
+        return _time_matrix(mat, m, reps)
+
+
+def _time_matrix(mat, m, reps):
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
     x = torch.randn((m, mat.k), device="cuda").half()
@@ -219,7 +254,8 @@ def decode_step(ms=(1, 2, 4, 8), reps=3):
     """The synthetic decode step of a ~27B dense decoder: 64 layers of
     [qkv FP8, o_proj FP8, gate_up NVFP4, down NVFP4], then the NVFP4 lm_head,
     each layer's weights at their own addresses (14.1 GB in all), launched in
-    order as one HIP graph. Returns {m: (ms per step, aggregate GB/s)}."""
+    order, once from the host one launch at a time and once as one HIP graph.
+    Returns {m: (graph ms per step, graph GB/s, bytes, stream-ordered ms)}."""
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
     wl = "decode_step_27b"
@@ -246,20 +282,34 @@ def decode_step(ms=(1, 2, 4, 8), reps=3):
         x, y, ws = bufs["lm_head"]
         launches.append(lambda x=x, c=head.copies[0], y=y, ws=ws: qt.gemm(x, c, out=y, workspace=ws))
         total += head.bytes_for(m)
-        g = capture(launches)
-        g.replay()
-        torch.cuda.synchronize()
         s = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        for _ in range(reps):
+        # stream-ordered: the launches issued one by one from the host
+        with mark(f"decode_m{m}/stream"):
+            for fn in launches:
+                fn()
+            torch.cuda.synchronize()
+            e0.record(s)
+            for _ in range(reps):
+                for fn in launches:
+                    fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+        ms_stream = e0.elapsed_time(e1) / reps
+        # one HIP graph holding the whole step
+        with mark(f"decode_m{m}/graph"):
+            g = capture(launches)
             g.replay()
-        e1.record(s)
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+            torch.cuda.synchronize()
         ms_step = e0.elapsed_time(e1) / reps
-        out[m] = (ms_step, total / (ms_step * 1e-3) / 1e9, total)
-        log(f"decode step M={m}: {ms_step:.3f} ms, {out[m][1]:.0f} GB/s over {total / 1e9:.2f} GB "
-            f"({len(launches)} GEMMs)")
+        out[m] = (ms_step, total / (ms_step * 1e-3) / 1e9, total, ms_stream)
+        log(f"decode step M={m}: graph {ms_step:.3f} ms, {out[m][1]:.0f} GB/s; stream-ordered {ms_stream:.3f} ms, "
+            f"{total / (ms_stream * 1e-3) / 1e9:.0f} GB/s; {total / 1e9:.2f} GB, {len(launches)} GEMMs")
         del g
     del protos, head
     torch.cuda.empty_cache()
@@ -314,7 +364,8 @@ def main():
     from quantized_weight_skinny_amd import torch_api as qt  # noqa: F401  (fails loudly without libqpn.so)
 
     log("read ceiling")
-    ceiling, ceiling_grid = read_ceiling()
+    with mark("read_ceiling/4GiB"):
+        ceiling, ceiling_grid = read_ceiling()
     log(f"ceiling {ceiling:.0f} GB/s (grid {ceiling_grid})")
 
     log("building rotating weights for the M=1 MLP step")
@@ -345,18 +396,20 @@ def main():
     eager_y = y.clone()
     warm = capture([(lambda i=i: step(i)) for i in range(max(args.warmup, 1))])
     timed = capture([(lambda i=i: step(i)) for i in range(args.steps)])
-    warm.replay()
-    torch.cuda.synchronize()
+    with mark("step/warmup"):
+        warm.replay()
+        torch.cuda.synchronize()
     if not torch.equal(y, eager_y):
         raise SystemExit("graph replay does not reproduce the eager step")
     s = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record(s)
-    timed.replay()
-    t1.record(s)
-    torch.cuda.synchronize()
+    with mark("step/timed"):
+        t0.record(s)
+        timed.replay()
+        t1.record(s)
+        torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -364,7 +417,7 @@ def main():
 
     # The dominant kernel (gate_up): a graph of back-to-back launches over
     # the rotating copies, events on the launch stream around it.
-    gate_up_us, achieved = time_matrix(gate_up, m, reps=2)
+    gate_up_us, achieved = time_matrix(gate_up, m, reps=2, label="roofline/nvfp4_m1/gate_up")
     traffic = kernel_traffic()
     log(f"step {ms_step * 1e3:.1f} us, {value:.0f} GB/s; gate_up {gate_up_us:.1f} us per launch, "
         f"{achieved:.0f} GB/s; wall {wall:.3f} s; traffic {traffic}")
@@ -374,13 +427,16 @@ def main():
     same_size = read_ceiling_sized(gate_up.weight_bytes)
     log(f"read ceiling at gate_up size: {same_size:.0f} GB/s")
 
-    extras = {}
-    if not args.no_extras:
+    extras, same_size_ceilings = {}, {"gate_up": round(same_size, 1)}
+    decode = None
+    if not args.quick:
         per = {}
         per["nvfp4_m1/gate_up"] = time_matrix(gate_up, 1)
         per["nvfp4_m1/down"] = time_matrix(down, 1)
         per["nvfp4_m8/gate_up"] = time_matrix(gate_up, 8)
         per["nvfp4_m8/down"] = time_matrix(down, 8)
+        per["nvfp4_m16/gate_up"] = time_matrix(gate_up, 16)
+        per["nvfp4_m16/down"] = time_matrix(down, 16)
         del gate_up, down
         torch.cuda.empty_cache()
         for name in ("qkv", "o_proj"):
@@ -388,22 +444,49 @@ def main():
             per[f"nvfp4_m8/{name}"] = time_matrix(mat, 8)
             del mat
             torch.cuda.empty_cache()
-        if args.all:
-            for name in ("qkv", "down"):
-                mat = Mat(name, "fp8", "fp8_27b_m124")
-                for mm in (1, 2, 4):
-                    per[f"fp8_m{mm}/{name}"] = time_matrix(mat, mm)
-                del mat
-                torch.cuda.empty_cache()
+        for name in ("qkv", "down", "o_proj"):
+            mat = Mat(name, "fp8", "fp8_27b_m124")
+            for mm in (1, 2, 4):
+                per[f"fp8_m{mm}/{name}"] = time_matrix(mat, mm)
+            del mat
+            torch.cuda.empty_cache()
+        mat = Mat("gemv", "nvfp4", "nvfp4_gemv_m1")
+        per["nvfp4_m1/gemv"] = time_matrix(mat, 1)
+        del mat
+        for name in ("qkv_tp4", "o_proj_tp4", "gate_up_tp4", "down_tp4"):
+            mat = Mat(name, "nvfp4", "nvfp4_27b_tp4")
+            for mm in (1, 8):
+                per[f"nvfp4_m{mm}/{name}"] = time_matrix(mat, mm)
+            del mat
+            torch.cuda.empty_cache()
+        head = Mat("lm_head", "nvfp4", "decode_step_27b", copies=6)
+        per["nvfp4_m1/lm_head"] = time_matrix(head, 1)
+        per["nvfp4_m8/lm_head"] = time_matrix(head, 8)
+        del head
+        torch.cuda.empty_cache()
         for key, (us, gbps) in per.items():
             extras[key] = {"us": round(us, 2), "GBps": round(gbps, 1),
                            "frac_of_measured_ceiling": round(gbps / ceiling, 4)}
             log(f"{key}: {us:.1f} us {gbps:.0f} GB/s ({100 * gbps / ceiling:.1f}% of ceiling)")
-
-    decode = None
-    if args.all:
+        # the read kernel at the size of the other large matrices, for
+        # comparing each GEMM with a plain read of its own size
+        for name, fmt in (("down", "nvfp4"), ("qkv", "fp8"), ("o_proj", "nvfp4")):
+            n, k = workloads.SHAPES[name]
+            nbytes = n * k // 2 + n * k // 16 if fmt == "nvfp4" else n * k + 4 * n
+            same_size_ceilings[f"{name}_{fmt}"] = round(read_ceiling_sized(nbytes), 1)
+            log(f"read ceiling at {name} {fmt} size ({nbytes / 1e6:.1f} MB): "
+                f"{same_size_ceilings[f'{name}_{fmt}']:.0f} GB/s")
+        same_of = {"gate_up": "gate_up", "down": "down_nvfp4", "o_proj": "o_proj_nvfp4"}
+        for key, row in extras.items():
+            fmt_m, name = key.split("/")
+            ref = "qkv_fp8" if (fmt_m.startswith("fp8") and name == "qkv") else \
+                (same_of.get(name) if fmt_m.startswith("nvfp4") else None)
+            if ref in same_size_ceilings:
+                row["frac_of_same_size_read"] = round(row["GBps"] / same_size_ceilings[ref], 4)
         decode = {str(m): {"ms_per_step": round(v[0], 4), "GBps": round(v[1], 1),
-                           "weight_and_io_bytes": v[2], "frac_of_measured_ceiling": round(v[1] / ceiling, 4)}
+                           "weight_and_io_bytes": v[2], "frac_of_measured_ceiling": round(v[1] / ceiling, 4),
+                           "stream_ordered_ms_per_step": round(v[3], 4),
+                           "stream_ordered_GBps": round(v[2] / (v[3] * 1e-3) / 1e9, 1)}
                   for m, v in decode_step().items()}
 
     cpu = None
@@ -438,6 +521,7 @@ def main():
                      "launch_us": round(gate_up_us, 3), "algorithmic_bytes": gate_up_bytes},
         "measured_read_ceiling_GBps": round(ceiling, 1),
         "read_ceiling_at_gate_up_size_GBps": round(same_size, 1),
+        "read_ceiling_same_size_GBps": same_size_ceilings,
         "frac_of_measured_ceiling": round(value / ceiling, 4),
         "cpu_baseline": cpu,
         "per_matrix": extras,

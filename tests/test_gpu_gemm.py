@@ -204,6 +204,8 @@ FULL = [
     ("fp8", "qkv", 1), ("fp8", "qkv", 4), ("fp8", "qkv", 8), ("fp8", "down", 2), ("fp8", "down", 4),
     ("fp8", "down", 7), ("fp8", "o_proj", 1), ("fp8", "o_proj", 4), ("fp8", "o_proj", 8),
     ("nvfp4", "lm_head", 1), ("nvfp4", "lm_head", 8),
+    ("nvfp4", "gate_up", 16), ("nvfp4", "down", 16), ("fp8", "o_proj", 2), ("nvfp4", "gemv", 1),
+    ("nvfp4", "qkv_tp4", 1), ("nvfp4", "o_proj_tp4", 8), ("nvfp4", "gate_up_tp4", 8), ("nvfp4", "down_tp4", 1),
 ]
 
 

@@ -30,6 +30,13 @@ SHAPES = {
     "qkv": (7168, 5120),
     "o_proj": (5120, 5120),
     "lm_head": (151936, 5120),
+    # one GPU's share of each matrix under 4-way tensor parallelism: the
+    # column-parallel ones (qkv, gate_up) cut along N, the row-parallel ones
+    # (o_proj, down) along K
+    "qkv_tp4": (1792, 5120),
+    "o_proj_tp4": (5120, 1280),
+    "gate_up_tp4": (8704, 5120),
+    "down_tp4": (5120, 4352),
 }
 
 # Workloads by name: (format, M values, matrices).
@@ -40,6 +47,9 @@ WORKLOADS = {
     "fp8_27b_m124": ("fp8", (1, 2, 4), ("qkv", "down")),
     # 64 layers of [qkv FP8, o_proj FP8, gate_up NVFP4, down NVFP4] + NVFP4 lm_head
     "decode_step_27b": ("mixed", (1, 2, 4, 8), ("qkv", "o_proj", "gate_up", "down", "lm_head")),
+    # per-rank shapes of 4-way tensor parallelism, and the 16-row verify block
+    "nvfp4_27b_tp4": ("nvfp4", (1, 8), ("qkv_tp4", "o_proj_tp4", "gate_up_tp4", "down_tp4")),
+    "nvfp4_27b_m16": ("nvfp4", (16,), ("gate_up", "down")),
 }
 
 DECODE_LAYERS = 64
