@@ -23,7 +23,8 @@ compromise."). Such a kernel reaches, up to summation order, the plain result
 where wdq is the dequantized weight. The oracle writes that definition out in
 float64 (``gemm.py``), together with the format tables and encoders
 (``formats.py``), the quantizers that produce synthetic NVFP4 / FP8 weights
-(``quantize.py``) and the canonical byte layout of packed codes (``layout.py``).
+(``quantize.py``), the canonical byte layout of packed codes (``layout.py``)
+and the SwiGLU that a fused gate_up epilogue computes (``mlp.py``).
 
 The pages never define the bit formats; the oracle uses the public
 definitions: E2M1 (OCP Microscaling spec v1.0, FP4 element type), E4M3 "FN"
@@ -59,11 +60,12 @@ from .gemm import (
     gemm_fp8,
     tolerance,
 )
+from .mlp import silu, split_gate_up, swiglu, swiglu_tolerance
 
 __all__ = [
     "E2M1_MAX", "E4M3_MAX", "e2m1_table", "e4m3_table", "decode_e2m1",
     "decode_e4m3", "encode_e2m1", "encode_e4m3", "quantize_nvfp4",
     "quantize_fp8", "nvfp4_tensor_scale", "pack_nibbles", "unpack_nibbles",
     "dequantize_nvfp4", "dequantize_fp8", "skinny_gemm", "gemm_nvfp4",
-    "gemm_fp8", "tolerance",
+    "gemm_fp8", "tolerance", "silu", "split_gate_up", "swiglu", "swiglu_tolerance",
 ]
