@@ -108,8 +108,8 @@ class Mat:
             self.copies.append(qt.PackedWeight(pw.fmt, n, k, pw.packed.clone(), pw.tensor_scale, rs))
         torch.cuda.synchronize()
 
-    def bytes_for(self, m):
-        return self.weight_bytes + 2 * m * self.k + 2 * m * self.n
+    def bytes_for(self, m, swiglu=False):
+        return self.weight_bytes + 2 * m * self.k + 2 * m * (self.n // 2 if swiglu else self.n)
 
 
 def capture(launches):
@@ -126,20 +126,22 @@ def capture(launches):
     return g
 
 
-def time_matrix(mat, m, reps=3, label=None):
+def time_matrix(mat, m, reps=3, label=None, swiglu=False):
     """Average µs per launch of one matrix: a graph of back-to-back launches
-    over all rotating copies, timed with events on the launch stream."""
-    with mark(label or f"{mat.fmt}_m{m}/{mat.name}"):
-        return _time_matrix(mat, m, reps)
+    over all rotating copies, timed with events on the launch stream.
+    ``swiglu``: the gate_up GEMM with the SwiGLU epilogue (output n/2 wide)."""
+    with mark(label or f"{mat.fmt}_m{m}/{mat.name}{'_swiglu' if swiglu else ''}"):
+        return _time_matrix(mat, m, reps, swiglu)
 
 
-def _time_matrix(mat, m, reps):
+def _time_matrix(mat, m, reps, swiglu=False):
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
     x = torch.randn((m, mat.k), device="cuda").half()
-    y = torch.empty((m, mat.n), dtype=torch.float16, device="cuda")
-    ws = qt.new_workspace(mat.copies[0], m)
-    launches = [(lambda c=c: qt.gemm(x, c, out=y, workspace=ws)) for c in mat.copies]
+    y = torch.empty((m, mat.n // 2 if swiglu else mat.n), dtype=torch.float16, device="cuda")
+    ws = qt.new_workspace(mat.copies[0], m, swiglu=swiglu)
+    run = qt.gemm_swiglu if swiglu else qt.gemm
+    launches = [(lambda c=c: run(x, c, out=y, workspace=ws)) for c in mat.copies]
     for fn in launches:
         fn()
     g = capture(launches)
@@ -154,7 +156,43 @@ def _time_matrix(mat, m, reps):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * len(launches))
     del g
-    return us, mat.bytes_for(m) / (us * 1e-6) / 1e9
+    return us, mat.bytes_for(m, swiglu) / (us * 1e-6) / 1e9
+
+
+def time_mlp(gate_up, down, m, reps=3):
+    """The MLP of one layer as the decoder runs it: x -> gate_up with the
+    SwiGLU epilogue -> h -> down -> y, over the rotating copies, one graph.
+    Returns (µs per MLP, GB/s over weights + x + h written and read + y)."""
+    import torch
+    from quantized_weight_skinny_amd import torch_api as qt
+    with mark(f"nvfp4_m{m}/mlp_swiglu"):
+        x = torch.randn((m, gate_up.k), device="cuda").half()
+        h = torch.empty((m, gate_up.n // 2), dtype=torch.float16, device="cuda")
+        y = torch.empty((m, down.n), dtype=torch.float16, device="cuda")
+        ws_g = qt.new_workspace(gate_up.copies[0], m, swiglu=True)
+        ws_d = qt.new_workspace(down.copies[0], m)
+        r = min(len(gate_up.copies), len(down.copies))
+
+        def mlp(i):
+            qt.gemm_swiglu(x, gate_up.copies[i], out=h, workspace=ws_g)
+            qt.gemm(h, down.copies[i], out=y, workspace=ws_d)
+
+        for i in range(r):
+            mlp(i)
+        g = capture([(lambda i=i: mlp(i)) for i in range(r)])
+        g.replay()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * r)
+        del g
+    nbytes = gate_up.bytes_for(m, swiglu=True) + down.bytes_for(m)
+    return us, nbytes / (us * 1e-6) / 1e9
 
 
 def read_ceiling(nbytes=4 << 30, reps=6):
@@ -437,6 +475,9 @@ def main():
         per["nvfp4_m8/down"] = time_matrix(down, 8)
         per["nvfp4_m16/gate_up"] = time_matrix(gate_up, 16)
         per["nvfp4_m16/down"] = time_matrix(down, 16)
+        for mm in (1, 8):
+            per[f"nvfp4_m{mm}/gate_up_swiglu"] = time_matrix(gate_up, mm, swiglu=True)
+            per[f"nvfp4_m{mm}/mlp_swiglu"] = time_mlp(gate_up, down, mm)
         del gate_up, down
         torch.cuda.empty_cache()
         for name in ("qkv", "o_proj"):
@@ -476,7 +517,7 @@ def main():
             same_size_ceilings[f"{name}_{fmt}"] = round(read_ceiling_sized(nbytes), 1)
             log(f"read ceiling at {name} {fmt} size ({nbytes / 1e6:.1f} MB): "
                 f"{same_size_ceilings[f'{name}_{fmt}']:.0f} GB/s")
-        same_of = {"gate_up": "gate_up", "down": "down_nvfp4", "o_proj": "o_proj_nvfp4"}
+        same_of = {"gate_up": "gate_up", "gate_up_swiglu": "gate_up", "down": "down_nvfp4", "o_proj": "o_proj_nvfp4"}
         for key, row in extras.items():
             fmt_m, name = key.split("/")
             ref = "qkv_fp8" if (fmt_m.startswith("fp8") and name == "qkv") else \

@@ -167,8 +167,8 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
                     void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
- * An explicit launch shape for qpn_gemm_tuned (tuning sweeps). 0 in any
- * field means "choose automatically".
+ * An explicit launch shape for qpn_gemm_tuned (tuning sweeps), and the
+ * epilogue. 0 in any shape field means "choose automatically".
  *   split_k          cut K into this many ranges over workgroups (their fp32
  *                    partials are added by the last workgroup to finish);
  *   waves_per_group  4 or 8 wavefronts per workgroup;
@@ -176,14 +176,19 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *                    wavefront;
  *   k_slices         1, 2, 4 or 8 (at most waves_per_group): wavefronts of
  *                    one workgroup that split one n-tile's K range and add
- *                    their results through LDS.
+ *                    their results through LDS;
+ *   epilogue         QPN_EPILOGUE_NONE (y as in qpn_gemm) or
+ *                    QPN_EPILOGUE_SWIGLU (see qpn_gemm_swiglu).
  */
+typedef enum { QPN_EPILOGUE_NONE = 0, QPN_EPILOGUE_SWIGLU = 1 } qpn_epilogue;
+
 typedef struct {
   int32_t split_k;
   int32_t waves_per_group;
   int32_t depth;
   int32_t k_slices;
-  int32_t reserved[4]; /* must be 0 */
+  int32_t epilogue;
+  int32_t reserved[3]; /* must be 0 */
 } qpn_launch;
 
 /* qpn_gemm with an explicit launch shape (NULL = automatic). A shape whose
@@ -199,6 +204,22 @@ size_t qpn_workspace_bytes_tuned(const qpn_weight* w, int32_t m, const qpn_launc
  * resolved (launch NULL = what qpn_gemm uses): written to *resolved. Returns
  * QPN_ERR_UNSUPPORTED for a shape that is not possible; no device work. */
 qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launch, qpn_launch* resolved);
+
+/*
+ * The gate_up GEMM of a gated MLP with SwiGLU fused into its epilogue. The
+ * weight is the row concatenation [W_gate; W_up] (w->n = 2 * F, F a multiple
+ * of 16); with g = x W_gate^T and u = x W_up^T (fp32 accumulators, scaled),
+ * the output is
+ *   h_dev     fp16 [m][F] row-major, h = silu(g) * u, silu(g) = g / (1 + e^-g),
+ *             rounded once to fp16 (fully overwritten), 2-byte aligned,
+ * so the N x M gate_up result never goes to memory. Other arguments as in
+ * qpn_gemm; the workspace is qpn_workspace_bytes_tuned(w, m, launch) with
+ * launch->epilogue = QPN_EPILOGUE_SWIGLU. w->n not a multiple of 32 returns
+ * QPN_ERR_INVALID_ARG. (The SwiGLU between the two projections is not
+ * described on the pages; this is the common fused gate_up form.)
+ */
+qpn_status qpn_gemm_swiglu(const void* x_dev, const qpn_weight* w, void* h_dev, int32_t m,
+                           void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
  * Read-only streaming kernel that measures the HBM read ceiling the GEMM is

@@ -28,6 +28,9 @@ QPN_FMT_NVFP4 = 1
 QPN_FMT_FP8_E4M3 = 2
 QPN_MAX_M = 16
 
+QPN_EPILOGUE_NONE = 0
+QPN_EPILOGUE_SWIGLU = 1
+
 
 class QpnError(RuntimeError):
     def __init__(self, status, where):
@@ -41,7 +44,8 @@ class qpn_launch(ctypes.Structure):
         ("waves_per_group", ctypes.c_int32),
         ("depth", ctypes.c_int32),
         ("k_slices", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("epilogue", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -82,6 +86,7 @@ SIGNATURES = {
     "qpn_gemm_plan": (_I32, [_W, _I32, _L, _L]),
     "qpn_gemm": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
     "qpn_gemm_tuned": (_I32, [_P, _W, _P, _I32, _P, _SZ, _L, _P]),
+    "qpn_gemm_swiglu": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
     "qpn_read_ceiling": (_I32, [_P, _SZ, _P, _I32, _P]),
     "qpn_read_ceiling_grid": (_I32, []),
 }
@@ -162,8 +167,8 @@ def qpn_workspace_bytes(weight, m):
     return lib().qpn_workspace_bytes(ctypes.byref(weight), m)
 
 
-def make_launch(split_k=0, waves_per_group=0, depth=0, k_slices=0):
-    return qpn_launch(split_k, waves_per_group, depth, k_slices)
+def make_launch(split_k=0, waves_per_group=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE):
+    return qpn_launch(split_k, waves_per_group, depth, k_slices, epilogue)
 
 
 def qpn_workspace_bytes_tuned(weight, m, launch):
@@ -187,6 +192,11 @@ def qpn_gemm_tuned(x, weight, y, m, workspace, workspace_bytes, launch, stream):
     return _check(lib().qpn_gemm_tuned(x, ctypes.byref(weight), y, m, workspace, workspace_bytes,
                                        ctypes.byref(launch) if launch is not None else None, stream),
                   "qpn_gemm_tuned")
+
+
+def qpn_gemm_swiglu(x, weight, h, m, workspace, workspace_bytes, stream):
+    return _check(lib().qpn_gemm_swiglu(x, ctypes.byref(weight), h, m, workspace, workspace_bytes, stream),
+                  "qpn_gemm_swiglu")
 
 
 def qpn_read_ceiling(buf, nbytes, sink, grid, stream):

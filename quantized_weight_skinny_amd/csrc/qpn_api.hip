@@ -136,13 +136,15 @@ namespace {
 
 bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   if (!l) return true;
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 3; ++i)
     if (l->reserved[i] != 0) return false;
   if (l->split_k < 0 || l->waves_per_group < 0 || l->depth < 0 || l->k_slices < 0) return false;
+  if (l->epilogue != QPN_EPILOGUE_NONE && l->epilogue != QPN_EPILOGUE_SWIGLU) return false;
   o->split = l->split_k;
   o->waves = l->waves_per_group;
   o->depth = l->depth;
   o->k_slices = l->k_slices;
+  o->swiglu = l->epilogue == QPN_EPILOGUE_SWIGLU;
   return true;
 }
 
@@ -173,6 +175,7 @@ qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launc
   resolved->waves_per_group = p.waves;
   resolved->depth = p.depth;
   resolved->k_slices = p.k_slices;
+  resolved->epilogue = p.swiglu ? QPN_EPILOGUE_SWIGLU : QPN_EPILOGUE_NONE;
   return QPN_OK;
 }
 
@@ -189,6 +192,7 @@ qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, i
     return QPN_ERR_INVALID_ARG;
   if (o.k_slices != 0 && o.k_slices != 1 && o.k_slices != 2 && o.k_slices != 4 && o.k_slices != 8)
     return QPN_ERR_INVALID_ARG;
+  if (o.swiglu && w->n % 32) return QPN_ERR_INVALID_ARG;
   if (m == 0 || w->n == 0) return QPN_OK;
   if (!y_dev || !aligned(y_dev, 2)) return QPN_ERR_INVALID_ARG;
   if (w->k > 0) {
@@ -211,6 +215,13 @@ qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, i
 qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
                     void* workspace_dev, size_t workspace_bytes, void* stream) {
   return qpn_gemm_tuned(x_dev, w, y_dev, m, workspace_dev, workspace_bytes, nullptr, stream);
+}
+
+qpn_status qpn_gemm_swiglu(const void* x_dev, const qpn_weight* w, void* h_dev, int32_t m,
+                           void* workspace_dev, size_t workspace_bytes, void* stream) {
+  qpn_launch l{};
+  l.epilogue = QPN_EPILOGUE_SWIGLU;
+  return qpn_gemm_tuned(x_dev, w, h_dev, m, workspace_dev, workspace_bytes, &l, stream);
 }
 
 int32_t qpn_read_ceiling_grid(void) { return qpn::read_ceiling_default_grid(); }

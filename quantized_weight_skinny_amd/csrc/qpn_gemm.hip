@@ -103,6 +103,28 @@ __device__ __forceinline__ void lds_dma16(const void* src, _Float16* lds_dst) {
 
 __device__ __forceinline__ h8 x_fragment(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
 
+// silu(g) = g / (1 + e^-g) in fp32 (e^-g overflows to +inf for g < -88,
+// giving -0, the limit).
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// Sum over the S K ranges of one output's fp32 partials (stride apart), in
+// range order. The partials are fetched kFixupBatch at a time, all loads of a
+// batch in flight together: one memory round trip per batch, not per range.
+__device__ __forceinline__ float range_sum(const float* src, size_t stride, int S) {
+  float sum = 0.f;
+  for (int r0 = 0; r0 < S; r0 += kFixupBatch) {
+    float part[kFixupBatch];
+#pragma unroll
+    for (int j = 0; j < kFixupBatch; ++j)
+      part[j] = r0 + j < S ? __hip_atomic_load(src + (r0 + j) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+#pragma unroll
+    for (int j = 0; j < kFixupBatch; ++j)
+      if (r0 + j < S) sum += part[j];
+  }
+  return sum;
+}
+
 // The eight MFMA steps of a unit alternate between two accumulators, which
 // halves the chain of dependent matrix instructions per wavefront; the two
 // are added once at the end (a fixed order, so results stay reproducible).
@@ -130,12 +152,15 @@ __device__ __forceinline__ void unit_mfma(const Unit<kFmtFp8>& w, const _Float16
   }
 }
 
-template <int FMT, int WAVES, int DEPTH>
+template <int FMT, int WAVES, int DEPTH, bool SWIGLU>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     const _Float16* __restrict__ x, const uint8_t* packed,
     const float* __restrict__ row_scales, float tensor_scale, _Float16* __restrict__ y,
     float* __restrict__ ws, int* __restrict__ counters, int M, int N, int K, int NT, int KU, int ups,
     int stride, int KS) {
+  // SWIGLU (a template parameter, so the plain kernels carry none of it):
+  // output h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:], see the epilogues.
+  constexpr bool swiglu = SWIGLU;
   extern __shared__ __align__(16) _Float16 xs[];
   __shared__ int last_group;
   constexpr int kBytes = Unit<FMT>::kBytes;
@@ -154,8 +179,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   const int sub = (nu + KS - 1) / KS;
   const int wu0 = min(ks * sub, nu);
   const int wnu = min(sub, nu - wu0);
-  const int nt = blockIdx.x * TN + tn;
-  const bool active = nt < NT;
+  // With the SwiGLU epilogue the workgroup pairs gate and up n-tiles: its
+  // first TN/2 wavefront columns take gate tiles (rows below N/2), the
+  // others the up tiles holding the same rows + N/2.
+  const int half_tn = TN / 2;
+  const int NTh = NT / 2;
+  const int pair = blockIdx.x * half_tn + (tn < half_tn ? tn : tn - half_tn);
+  const int nt = swiglu ? (tn < half_tn ? pair : NTh + pair) : blockIdx.x * TN + tn;
+  const bool active = swiglu ? pair < NTh : nt < NT;
   const uint32_t unit_stride = static_cast<uint32_t>(NT) * kBytes;
   const Stream stream(packed + unit_offset(active ? nt : 0, u0 + wu0, NT, kBytes),
                       active && wnu > 0 ? static_cast<uint32_t>(wnu - 1) * unit_stride + kBytes : 0u,
@@ -252,6 +283,35 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
 
   // Lane (m = lane % 16, g = lane / 16) holds rows n = 4g + r of column m.
   const int n0 = nt * kTileN + g * 4;
+  const int Nh = N / 2;
+  if (S == 1 && swiglu) {
+    // The up wavefronts hand their scaled tiles to the gate wavefronts
+    // through LDS (the activation stage is dead), which write
+    // h = silu(gate) * up, rounded once to fp16.
+    f4* xch = reinterpret_cast<f4*>(xs);
+    __syncthreads();
+    if (ks == 0 && tn >= half_tn) {
+      f4 u = acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        u[r] *= FMT == kFmtNvfp4 ? tensor_scale : (n0 + r < N ? row_scales[n0 + r] : 0.f);
+      xch[(tn - half_tn) * 64 + lane] = u;
+    }
+    __syncthreads();
+    if (owner && tn < half_tn && mcol < M) {
+      const f4 u = xch[tn * 64 + lane];
+      _Float16* dst = y + static_cast<size_t>(mcol) * Nh;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = n0 + r;
+        if (n < Nh) {
+          const float gv = acc[r] * (FMT == kFmtNvfp4 ? tensor_scale : row_scales[n]);
+          dst[n] = static_cast<_Float16>(silu(gv) * u[r]);
+        }
+      }
+    }
+    return;
+  }
   if (S == 1) {
     if (owner && mcol < M) {
       _Float16* dst = y + static_cast<size_t>(mcol) * N;
@@ -293,37 +353,31 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
                  S - 1;
   __syncthreads();
   if (!last_group) return;
-  const int rows = TN * kTileN;
+  // Rows of the group: all TN tiles' rows, or (SwiGLU) the gate rows of its
+  // TN/2 gate tiles, each combined with its up row N/2 further on.
+  const int rows = (swiglu ? half_tn : TN) * kTileN;
   const int nbase = blockIdx.x * rows;
+  const int nend = swiglu ? Nh : N;
+  const size_t range_stride = static_cast<size_t>(M) * N;
   for (int idx = tid; idx < M * rows; idx += WAVES * 64) {
     const int m = idx / rows;
     const int n = nbase + (idx - m * rows);
-    if (n >= N) continue;
+    if (n >= nend) continue;
     const float* src = ws + static_cast<size_t>(m) * N + n;
-    const size_t range_stride = static_cast<size_t>(M) * N;
-    // The ranges' partials are fetched kFixupBatch at a time, all loads of a
-    // batch in flight together (one memory round trip per batch, not per
-    // range), and added in range order.
-    float sum = 0.f;
-    for (int r0 = 0; r0 < S; r0 += kFixupBatch) {
-      float part[kFixupBatch];
-#pragma unroll
-      for (int j = 0; j < kFixupBatch; ++j)
-        part[j] = r0 + j < S ? __hip_atomic_load(src + (r0 + j) * range_stride, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)
-                             : 0.f;
-#pragma unroll
-      for (int j = 0; j < kFixupBatch; ++j)
-        if (r0 + j < S) sum += part[j];
+    const float sum = range_sum(src, range_stride, S) * (FMT == kFmtNvfp4 ? tensor_scale : row_scales[n]);
+    if (swiglu) {
+      const float u = range_sum(src + Nh, range_stride, S) *
+                      (FMT == kFmtNvfp4 ? tensor_scale : row_scales[n + Nh]);
+      y[static_cast<size_t>(m) * Nh + n] = static_cast<_Float16>(silu(sum) * u);
+    } else {
+      y[static_cast<size_t>(m) * N + n] = static_cast<_Float16>(sum);
     }
-    const float scale = FMT == kFmtNvfp4 ? tensor_scale : row_scales[n];
-    y[static_cast<size_t>(m) * N + n] = static_cast<_Float16>(sum * scale);
   }
   if (tid == 0) __hip_atomic_store(counters + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int FMT, int WAVES, int DEPTH>
-hipError_t launch_cfg(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
+template <int FMT, int WAVES, int DEPTH, bool SWIGLU>
+hipError_t launch_cfg_e(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
                       float tensor_scale, void* y, void* workspace, int m, int64_t n, int64_t k,
                       hipStream_t stream) {
   const int NT = static_cast<int>(ceil_div(n, kTileN));
@@ -331,18 +385,28 @@ hipError_t launch_cfg(const GemmPlan& p, const void* x, const void* packed, cons
   const unsigned groups = static_cast<unsigned>(ceil_div(NT, WAVES / p.k_slices));
   // Dynamic LDS above the 64 KiB default must be allowed per kernel.
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH>),
+      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH, SWIGLU>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBudget));
   if (attr != hipSuccess) return attr;
   int* counters = p.split > 1 ? static_cast<int*>(workspace) : nullptr;
   float* ws = p.split > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.partials_offset)
                           : nullptr;
-  hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH>), dim3(groups, static_cast<unsigned>(p.split)),
+  hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH, SWIGLU>), dim3(groups, static_cast<unsigned>(p.split)),
                      dim3(WAVES * 64), p.lds_bytes, stream, static_cast<const _Float16*>(x),
                      static_cast<const uint8_t*>(packed), row_scales, tensor_scale,
                      static_cast<_Float16*>(y), ws, counters, m, static_cast<int>(n),
                      static_cast<int>(k), NT, KU, p.units_per_split, p.lds_stride, p.k_slices);
   return hipGetLastError();
+}
+
+template <int FMT, int WAVES, int DEPTH>
+hipError_t launch_cfg(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
+                      float tensor_scale, void* y, void* workspace, int m, int64_t n, int64_t k,
+                      hipStream_t stream) {
+  return p.swiglu ? launch_cfg_e<FMT, WAVES, DEPTH, true>(p, x, packed, row_scales, tensor_scale, y, workspace,
+                                                          m, n, k, stream)
+                  : launch_cfg_e<FMT, WAVES, DEPTH, false>(p, x, packed, row_scales, tensor_scale, y, workspace,
+                                                           m, n, k, stream);
 }
 
 template <int FMT, int WAVES>
@@ -402,9 +466,23 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
     waves = tn_target * ks < 4 ? 4 : tn_target * ks > 8 ? 8 : tn_target * ks;
     if (waves < ks) waves = ks;
   }
+  // The SwiGLU epilogue pairs gate and up n-tiles inside a workgroup, so it
+  // needs an even number of n-tiles per workgroup (and N/2 on a tile
+  // boundary): an automatic shape gives up K slices (or adds wavefronts) to
+  // get there.
+  if (o.swiglu) {
+    if (n % (2 * kTileN)) return false;
+    if (waves && ks && (waves / ks) % 2) {
+      if (o.k_slices && o.waves) return false;
+      if (!o.k_slices && ks > 1) ks /= 2;
+      else if (!o.waves && waves < 8) waves *= 2;
+      else return false;
+    }
+  }
   if (waves != 4 && waves != 8) return false;
   if (ks != 1 && ks != 2 && ks != 4 && ks != 8) return false;
   if (ks > waves) return false;
+  if (o.swiglu && (waves / ks) % 2) return false;
   const int depth = w.depth ? w.depth : 3;
   if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
 
@@ -418,6 +496,10 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   // K slices reduce through the same LDS: one 16x16 fp32 tile per wavefront.
   const size_t red_bytes = ks > 1 ? static_cast<size_t>(waves) * 64 * sizeof(f4) : 0;
   if (p->lds_bytes < red_bytes) p->lds_bytes = red_bytes;
+  // ... and (SwiGLU) the up tiles handed to the gate wavefronts.
+  const size_t xch_bytes = o.swiglu ? static_cast<size_t>(waves / ks / 2) * 64 * sizeof(f4) : 0;
+  if (p->lds_bytes < xch_bytes) p->lds_bytes = xch_bytes;
+  p->swiglu = o.swiglu ? 1 : 0;
   if (split > 1) {
     // Counters first, one per n-tile (enough for any grouping of n-tiles),
     // so that their place does not depend on m, split or workgroup shape and

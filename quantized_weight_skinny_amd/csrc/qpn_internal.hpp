@@ -14,6 +14,7 @@ namespace qpn {
 // order.
 struct LaunchOverride {
   int split = 0, waves = 0, depth = 0, k_slices = 0;  // 0 = automatic
+  int swiglu = 0;  // 1: the SwiGLU epilogue (output h[M, N/2])
 };
 
 struct GemmPlan {
@@ -21,6 +22,7 @@ struct GemmPlan {
   int waves;
   int k_slices;    // wavefronts of a workgroup that split one n-tile's K range
   int depth;       // units of the weight stream each wavefront keeps in flight
+  int swiglu;      // epilogue: 0 y[M, N]; 1 h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:]
   int units_per_split;
   int lds_stride;  // halves per staged activation row
   size_t lds_bytes;

@@ -8,6 +8,8 @@ returns the tensors it allocated. No arithmetic of the method happens here.
 import torch
 
 from . import (
+    QPN_EPILOGUE_NONE,
+    QPN_EPILOGUE_SWIGLU,
     QPN_ERR_BAD_CODE,
     QPN_FMT_FP8_E4M3,
     QPN_FMT_NVFP4,
@@ -149,35 +151,30 @@ def quantize_fp8(w):
     return codes, rs
 
 
-def _launch(split_k=0, waves=0, depth=0, k_slices=0):
-    if split_k or waves or depth or k_slices:
-        return make_launch(split_k, waves, depth, k_slices)
+def _launch(split_k=0, waves=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE):
+    if split_k or waves or depth or k_slices or epilogue:
+        return make_launch(split_k, waves, depth, k_slices, epilogue)
     return None
 
 
-def workspace_bytes(pw, m, split_k=0, waves=0, depth=0, k_slices=0):
-    launch = _launch(split_k, waves, depth, k_slices)
+def workspace_bytes(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False):
+    launch = _launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_SWIGLU if swiglu else QPN_EPILOGUE_NONE)
     d = pw.desc()
     return qpn_workspace_bytes_tuned(d, m, launch) if launch is not None else qpn_workspace_bytes(d, m)
 
 
-def new_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, device="cuda"):
+def new_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, device="cuda"):
     """A zeroed workspace for gemm(pw) with m rows (None when none is needed)."""
-    need = workspace_bytes(pw, m, split_k, waves, depth, k_slices)
+    need = workspace_bytes(pw, m, split_k, waves, depth, k_slices, swiglu)
     return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
 
 
-def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0):
-    """y[m, n] = x[m, k] @ dequant(W)^T in fp16 through qpn_gemm.
-
-    A workspace, when one is needed and not given, is allocated zeroed per
-    call; pass one from new_workspace() to reuse it across calls."""
+def _run(x, pw, out, workspace, launch, cols):
     _cuda(x, torch.float16, "x")
     m = x.shape[0]
     if out is None:
-        out = torch.empty((m, pw.n), dtype=torch.float16, device=x.device)
+        out = torch.empty((m, cols), dtype=torch.float16, device=x.device)
     d = pw.desc()
-    launch = _launch(split_k, waves, depth, k_slices)
     need = qpn_workspace_bytes_tuned(d, m, launch) if launch is not None else qpn_workspace_bytes(d, m)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
@@ -188,6 +185,22 @@ def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=
     else:
         qpn_gemm(x.data_ptr(), d, out.data_ptr(), m, ws_ptr, ws_bytes, _stream())
     return out
+
+
+def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0):
+    """y[m, n] = x[m, k] @ dequant(W)^T in fp16 through qpn_gemm.
+
+    A workspace, when one is needed and not given, is allocated zeroed per
+    call; pass one from new_workspace() to reuse it across calls."""
+    return _run(x, pw, out, workspace, _launch(split_k, waves, depth, k_slices), pw.n)
+
+
+def gemm_swiglu(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0):
+    """h[m, n/2] = silu(g) * u with [g | u] = x @ dequant(W)^T (W's first n/2
+    rows are the gate projection): the SwiGLU epilogue of qpn_gemm_tuned
+    (zero shape fields: the shape qpn_gemm_swiglu uses)."""
+    launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_SWIGLU)
+    return _run(x, pw, out, workspace, launch, pw.n // 2)
 
 
 def read_ceiling(buf, grid=0, sink=None):

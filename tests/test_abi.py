@@ -137,6 +137,32 @@ def test_plan_resolves_tuned_and_rule_based_launches():
         q.qpn_gemm_plan(_w(n=5120, k=17408), 8, q.make_launch(split_k=1))
 
 
+def test_swiglu_epilogue_plans_and_checks():
+    # gate_up at M=1 is tuned for one n-tile per workgroup; SwiGLU pairs gate
+    # and up tiles, so the resolved shape has an even number of them
+    sw = q.make_launch(epilogue=q.QPN_EPILOGUE_SWIGLU)
+    p = q.qpn_gemm_plan(_w(n=34816, k=5120), 1, sw)
+    assert p.epilogue == q.QPN_EPILOGUE_SWIGLU
+    assert (p.waves_per_group // p.k_slices) % 2 == 0
+    for m in (1, 2, 4, 8, 16):
+        p = q.qpn_gemm_plan(_w(n=1056, k=2304), m, sw)
+        assert (p.waves_per_group // p.k_slices) % 2 == 0
+    # the split (and so the workspace) is the plain GEMM's
+    w = _w(n=34816, k=5120)
+    assert q.qpn_workspace_bytes_tuned(w, 8, sw) == q.qpn_workspace_bytes(w, 8)
+    # N must split into two halves of whole 16-row tiles
+    assert q.lib().qpn_gemm_swiglu(FAKE, ctypes.byref(_w(n=48, k=256)), FAKE, 1, None, 0, None) == \
+        q.QPN_ERR_INVALID_ARG
+    # an explicit shape with an odd number of n-tiles per workgroup is refused
+    bad = q.make_launch(1, 4, 3, 4, q.QPN_EPILOGUE_SWIGLU)
+    assert q.lib().qpn_gemm_tuned(FAKE, ctypes.byref(_w(n=512, k=1024)), FAKE, 1, None, 0,
+                                  ctypes.byref(bad), None) == q.QPN_ERR_UNSUPPORTED
+    # unknown epilogue values are argument errors
+    odd = q.make_launch(epilogue=2)
+    assert q.lib().qpn_gemm_tuned(FAKE, ctypes.byref(_w()), FAKE, 1, None, 0, ctypes.byref(odd), None) == \
+        q.QPN_ERR_INVALID_ARG
+
+
 def test_pack_and_quantize_reject_bad_arguments():
     lib = q.lib()
     nv = q.qpn_packed_bytes(q.QPN_FMT_NVFP4, 32, 64)
