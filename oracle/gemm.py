@@ -73,3 +73,16 @@ def gemm_fp8(x, codes, row_scales):
 def tolerance(b):
     """Per-element acceptance bound 2e-3 * b + 1e-3 for a GEMM output."""
     return 2e-3 * np.asarray(b, dtype=np.float64) + 1e-3
+
+
+def argmax_candidates(y, b):
+    """For each row of a GEMM output, the indices that can be its argmax once
+    every element is known only to within the acceptance bound t = tolerance(b):
+    i qualifies when y[i] + t[i] >= max_j (y[j] - t[j]). (A greedy decoder
+    takes the largest logit; when two logits are closer than the bound, either
+    is a correct answer.) Returns a boolean mask of y's shape; each row has at
+    least the exact argmax."""
+    y = np.asarray(y, dtype=np.float64)
+    t = tolerance(b)
+    floor = np.max(y - t, axis=-1, keepdims=True)
+    return (y + t) >= floor

@@ -98,3 +98,33 @@ def test_one_hot_activation_reads_back_one_weight():
 def test_tolerance_formula():
     assert oracle.tolerance(0.0) == 1e-3
     assert np.isclose(oracle.tolerance(10.0), 0.021)
+
+
+def test_argmax_candidates_clear_winner_and_near_ties():
+    # b = 0 gives the bound 1e-3 on every element
+    y = np.array([[0.0, 5.0, 1.0, 4.9],        # clear winner: index 1 alone
+                  [2.0, 2.0015, -1.0, 1.9996],  # within 2e-3 of the top: 0, 1 and 3
+                  [-3.0, -3.0, -3.0, -3.0]])   # all equal: every index
+    b = np.zeros_like(y)
+    c = oracle.argmax_candidates(y, b)
+    assert c[0].tolist() == [False, True, False, False]
+    assert c[1].tolist() == [True, True, False, True]
+    assert c[2].all()
+    # the exact argmax always qualifies, and a wider bound only adds indices
+    rng = np.random.default_rng(3)
+    yy = rng.standard_normal((50, 300))
+    bb = rng.random((50, 300))
+    c1 = oracle.argmax_candidates(yy, bb)
+    assert c1[np.arange(50), yy.argmax(1)].all()
+    assert (oracle.argmax_candidates(yy, 3 * bb) >= c1).all()
+    # brute force on a small case: i qualifies iff some choice of values within the
+    # bounds makes i the largest
+    y3 = rng.standard_normal((200, 5)) * 2e-3
+    b3 = np.zeros_like(y3)
+    c3 = oracle.argmax_candidates(y3, b3)
+    t = 1e-3
+    for r in range(200):
+        for i in range(5):
+            best_i = y3[r, i] + t
+            others = np.delete(y3[r] - t, i)
+            assert c3[r, i] == (best_i >= others.max())
