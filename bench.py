@@ -108,8 +108,9 @@ class Mat:
             self.copies.append(qt.PackedWeight(pw.fmt, n, k, pw.packed.clone(), pw.tensor_scale, rs))
         torch.cuda.synchronize()
 
-    def bytes_for(self, m, swiglu=False):
-        return self.weight_bytes + 2 * m * self.k + 2 * m * (self.n // 2 if swiglu else self.n)
+    def bytes_for(self, m, swiglu=False, argmax=False):
+        out = 8 * m if argmax else 2 * m * (self.n // 2 if swiglu else self.n)
+        return self.weight_bytes + 2 * m * self.k + out
 
 
 def capture(launches):
@@ -126,22 +127,30 @@ def capture(launches):
     return g
 
 
-def time_matrix(mat, m, reps=3, label=None, swiglu=False):
+def time_matrix(mat, m, reps=3, label=None, swiglu=False, argmax=False):
     """Average µs per launch of one matrix: a graph of back-to-back launches
     over all rotating copies, timed with events on the launch stream.
-    ``swiglu``: the gate_up GEMM with the SwiGLU epilogue (output n/2 wide)."""
-    with mark(label or f"{mat.fmt}_m{m}/{mat.name}{'_swiglu' if swiglu else ''}"):
-        return _time_matrix(mat, m, reps, swiglu)
+    ``swiglu``: the gate_up GEMM with the SwiGLU epilogue (output n/2 wide);
+    ``argmax``: the greedy-argmax epilogue (an index and a value per row)."""
+    tag = "_swiglu" if swiglu else "_argmax" if argmax else ""
+    with mark(label or f"{mat.fmt}_m{m}/{mat.name}{tag}"):
+        return _time_matrix(mat, m, reps, swiglu, argmax)
 
 
-def _time_matrix(mat, m, reps, swiglu=False):
+def _time_matrix(mat, m, reps, swiglu=False, argmax=False):
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
     x = torch.randn((m, mat.k), device="cuda").half()
     y = torch.empty((m, mat.n // 2 if swiglu else mat.n), dtype=torch.float16, device="cuda")
-    ws = qt.new_workspace(mat.copies[0], m, swiglu=swiglu)
-    run = qt.gemm_swiglu if swiglu else qt.gemm
-    launches = [(lambda c=c: run(x, c, out=y, workspace=ws)) for c in mat.copies]
+    if argmax:
+        ws = qt.argmax_workspace(mat.copies[0], m)
+        idx = torch.empty(m, dtype=torch.int32, device="cuda")
+        val = torch.empty(m, dtype=torch.float32, device="cuda")
+        launches = [(lambda c=c: qt.gemm_argmax(x, c, idx=idx, val=val, workspace=ws)) for c in mat.copies]
+    else:
+        ws = qt.new_workspace(mat.copies[0], m, swiglu=swiglu)
+        run = qt.gemm_swiglu if swiglu else qt.gemm
+        launches = [(lambda c=c: run(x, c, out=y, workspace=ws)) for c in mat.copies]
     for fn in launches:
         fn()
     g = capture(launches)
@@ -156,7 +165,7 @@ def _time_matrix(mat, m, reps, swiglu=False):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * len(launches))
     del g
-    return us, mat.bytes_for(m, swiglu) / (us * 1e-6) / 1e9
+    return us, mat.bytes_for(m, swiglu, argmax) / (us * 1e-6) / 1e9
 
 
 def time_mlp(gate_up, down, m, reps=3):
@@ -503,6 +512,8 @@ def main():
         head = Mat("lm_head", "nvfp4", "decode_step_27b", copies=6)
         per["nvfp4_m1/lm_head"] = time_matrix(head, 1)
         per["nvfp4_m8/lm_head"] = time_matrix(head, 8)
+        per["nvfp4_m1/lm_head_argmax"] = time_matrix(head, 1, argmax=True)
+        per["nvfp4_m8/lm_head_argmax"] = time_matrix(head, 8, argmax=True)
         del head
         torch.cuda.empty_cache()
         for key, (us, gbps) in per.items():

@@ -142,11 +142,12 @@ qpn_status qpn_quantize_fp8(const float* w_dev, int64_t n, int64_t k,
                             uint8_t* codes_dev, float* row_scales_dev, void* stream);
 
 /* Device workspace qpn_gemm needs for this weight and row count (0 if none).
- * When K is split over several workgroups the workspace holds fp32 partial
- * sums and one arrival counter per group of n-tiles. The counters must be
- * zero before the first call that uses a workspace (allocate it zeroed);
- * every call leaves them zero again. Calls that run at the same time must
- * not share a workspace. */
+ * When K is split over several workgroups the workspace holds one arrival
+ * counter per n-tile and fp32 partial sums. The counters sit at offsets that
+ * depend only on the weight, so one workspace (sized for the largest m)
+ * serves calls with any m and epilogue. They must be zero before the first
+ * call that uses the workspace (allocate it zeroed); every call leaves them
+ * zero again. Calls that run at the same time must not share a workspace. */
 size_t qpn_workspace_bytes(const qpn_weight* w, int32_t m);
 
 /*
@@ -177,10 +178,11 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *   k_slices         1, 2, 4 or 8 (at most waves_per_group): wavefronts of
  *                    one workgroup that split one n-tile's K range and add
  *                    their results through LDS;
- *   epilogue         QPN_EPILOGUE_NONE (y as in qpn_gemm) or
- *                    QPN_EPILOGUE_SWIGLU (see qpn_gemm_swiglu).
+ *   epilogue         QPN_EPILOGUE_NONE (y as in qpn_gemm), QPN_EPILOGUE_SWIGLU
+ *                    (see qpn_gemm_swiglu) or QPN_EPILOGUE_ARGMAX (only with
+ *                    qpn_gemm_argmax and the workspace / plan queries).
  */
-typedef enum { QPN_EPILOGUE_NONE = 0, QPN_EPILOGUE_SWIGLU = 1 } qpn_epilogue;
+typedef enum { QPN_EPILOGUE_NONE = 0, QPN_EPILOGUE_SWIGLU = 1, QPN_EPILOGUE_ARGMAX = 2 } qpn_epilogue;
 
 typedef struct {
   int32_t split_k;
@@ -220,6 +222,25 @@ qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launc
  */
 qpn_status qpn_gemm_swiglu(const void* x_dev, const qpn_weight* w, void* h_dev, int32_t m,
                            void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * A greedy output head: the GEMM with, per activation row, the index and the
+ * value of its largest logit, so the m x N logits never go to memory (for an
+ * lm_head at N = 151936 that is 0.3-4.9 MB per step). The logits are the
+ * scaled fp32 accumulators (not rounded to fp16); among equal logits the
+ * smallest index wins, so the result is deterministic.
+ *   idx_dev   int32 [m] output, 4-byte aligned.
+ *   val_dev   fp32 [m] output (the largest logits), or NULL.
+ *   launch    NULL or a launch shape (its epilogue field 0 or
+ *             QPN_EPILOGUE_ARGMAX); other arguments as in qpn_gemm_tuned.
+ * The workspace is always needed: qpn_workspace_bytes_tuned(w, m, launch)
+ * with launch->epilogue = QPN_EPILOGUE_ARGMAX. Its counters must be zero
+ * before the first call, and every call leaves them zero.
+ * (The pages speak of a native 4-bit lm_head; folding the greedy argmax into
+ * it is a reading of how a verify step uses that head.)
+ */
+qpn_status qpn_gemm_argmax(const void* x_dev, const qpn_weight* w, int32_t* idx_dev, float* val_dev, int32_t m,
+                           void* workspace_dev, size_t workspace_bytes, const qpn_launch* launch, void* stream);
 
 /*
  * Read-only streaming kernel that measures the HBM read ceiling the GEMM is

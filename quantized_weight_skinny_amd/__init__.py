@@ -30,6 +30,7 @@ QPN_MAX_M = 16
 
 QPN_EPILOGUE_NONE = 0
 QPN_EPILOGUE_SWIGLU = 1
+QPN_EPILOGUE_ARGMAX = 2
 
 
 class QpnError(RuntimeError):
@@ -87,6 +88,7 @@ SIGNATURES = {
     "qpn_gemm": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
     "qpn_gemm_tuned": (_I32, [_P, _W, _P, _I32, _P, _SZ, _L, _P]),
     "qpn_gemm_swiglu": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
+    "qpn_gemm_argmax": (_I32, [_P, _W, _P, _P, _I32, _P, _SZ, _L, _P]),
     "qpn_read_ceiling": (_I32, [_P, _SZ, _P, _I32, _P]),
     "qpn_read_ceiling_grid": (_I32, []),
 }
@@ -197,6 +199,12 @@ def qpn_gemm_tuned(x, weight, y, m, workspace, workspace_bytes, launch, stream):
 def qpn_gemm_swiglu(x, weight, h, m, workspace, workspace_bytes, stream):
     return _check(lib().qpn_gemm_swiglu(x, ctypes.byref(weight), h, m, workspace, workspace_bytes, stream),
                   "qpn_gemm_swiglu")
+
+
+def qpn_gemm_argmax(x, weight, idx, val, m, workspace, workspace_bytes, launch, stream):
+    return _check(lib().qpn_gemm_argmax(x, ctypes.byref(weight), idx, val, m, workspace, workspace_bytes,
+                                        ctypes.byref(launch) if launch is not None else None, stream),
+                  "qpn_gemm_argmax")
 
 
 def qpn_read_ceiling(buf, nbytes, sink, grid, stream):

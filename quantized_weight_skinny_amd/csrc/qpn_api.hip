@@ -139,12 +139,13 @@ bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   for (int i = 0; i < 3; ++i)
     if (l->reserved[i] != 0) return false;
   if (l->split_k < 0 || l->waves_per_group < 0 || l->depth < 0 || l->k_slices < 0) return false;
-  if (l->epilogue != QPN_EPILOGUE_NONE && l->epilogue != QPN_EPILOGUE_SWIGLU) return false;
+  if (l->epilogue != QPN_EPILOGUE_NONE && l->epilogue != QPN_EPILOGUE_SWIGLU && l->epilogue != QPN_EPILOGUE_ARGMAX)
+    return false;
   o->split = l->split_k;
   o->waves = l->waves_per_group;
   o->depth = l->depth;
   o->k_slices = l->k_slices;
-  o->swiglu = l->epilogue == QPN_EPILOGUE_SWIGLU;
+  o->epilogue = l->epilogue;
   return true;
 }
 
@@ -175,26 +176,31 @@ qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launc
   resolved->waves_per_group = p.waves;
   resolved->depth = p.depth;
   resolved->k_slices = p.k_slices;
-  resolved->epilogue = p.swiglu ? QPN_EPILOGUE_SWIGLU : QPN_EPILOGUE_NONE;
+  resolved->epilogue = p.epilogue;
   return QPN_OK;
 }
 
-qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
-                          void* workspace_dev, size_t workspace_bytes, const qpn_launch* launch,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One GEMM call with launch override o: y_dev is the fp16 output (or, for
+// the argmax epilogue, the int32 indices, with the fp32 values in val_dev).
+qpn_status gemm_call(const void* x_dev, const qpn_weight* w, void* y_dev, float* val_dev, int32_t m,
+                     void* workspace_dev, size_t workspace_bytes, const qpn::LaunchOverride& o, void* stream) {
   const qpn_status st = check_weight(w);
   if (st != QPN_OK) return st;
   if (m < 0 || m > QPN_MAX_M) return QPN_ERR_INVALID_ARG;
-  qpn::LaunchOverride o;
-  if (!to_override(launch, &o)) return QPN_ERR_INVALID_ARG;
   if (o.waves != 0 && o.waves != 4 && o.waves != 8) return QPN_ERR_INVALID_ARG;
   if (o.depth != 0 && o.depth != 2 && o.depth != 3 && o.depth != 4 && o.depth != 6 && o.depth != 8)
     return QPN_ERR_INVALID_ARG;
   if (o.k_slices != 0 && o.k_slices != 1 && o.k_slices != 2 && o.k_slices != 4 && o.k_slices != 8)
     return QPN_ERR_INVALID_ARG;
-  if (o.swiglu && w->n % 32) return QPN_ERR_INVALID_ARG;
+  if (o.epilogue == QPN_EPILOGUE_SWIGLU && w->n % 32) return QPN_ERR_INVALID_ARG;
   if (m == 0 || w->n == 0) return QPN_OK;
-  if (!y_dev || !aligned(y_dev, 2)) return QPN_ERR_INVALID_ARG;
+  const size_t out_align = o.epilogue == QPN_EPILOGUE_ARGMAX ? 4 : 2;
+  if (!y_dev || !aligned(y_dev, out_align)) return QPN_ERR_INVALID_ARG;
+  if (val_dev && !aligned(val_dev, 4)) return QPN_ERR_INVALID_ARG;
   if (w->k > 0) {
     if (!x_dev || !aligned(x_dev, 16)) return QPN_ERR_INVALID_ARG;
     if (!w->packed || !aligned(w->packed, 16)) return QPN_ERR_INVALID_ARG;
@@ -209,7 +215,29 @@ qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, i
     if (workspace_bytes < p.workspace_bytes) return QPN_ERR_BUFFER_TOO_SMALL;
   }
   return from_hip(qpn::launch_gemm(w->format, p, x_dev, w->packed, w->row_scales, w->tensor_scale,
-                                   y_dev, workspace_dev, m, w->n, w->k, as_stream(stream)));
+                                   y_dev, val_dev, workspace_dev, m, w->n, w->k, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
+                          void* workspace_dev, size_t workspace_bytes, const qpn_launch* launch,
+                          void* stream) {
+  qpn::LaunchOverride o;
+  if (!to_override(launch, &o)) return QPN_ERR_INVALID_ARG;
+  if (o.epilogue == QPN_EPILOGUE_ARGMAX) return QPN_ERR_INVALID_ARG;  // two outputs: qpn_gemm_argmax
+  return gemm_call(x_dev, w, y_dev, nullptr, m, workspace_dev, workspace_bytes, o, stream);
+}
+
+qpn_status qpn_gemm_argmax(const void* x_dev, const qpn_weight* w, int32_t* idx_dev, float* val_dev, int32_t m,
+                           void* workspace_dev, size_t workspace_bytes, const qpn_launch* launch, void* stream) {
+  qpn::LaunchOverride o;
+  if (!to_override(launch, &o)) return QPN_ERR_INVALID_ARG;
+  if (o.epilogue != QPN_EPILOGUE_NONE && o.epilogue != QPN_EPILOGUE_ARGMAX) return QPN_ERR_INVALID_ARG;
+  o.epilogue = QPN_EPILOGUE_ARGMAX;
+  return gemm_call(x_dev, w, idx_dev, val_dev, m, workspace_dev, workspace_bytes, o, stream);
 }
 
 qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,

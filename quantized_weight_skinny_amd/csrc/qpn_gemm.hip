@@ -80,6 +80,7 @@ const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
 }
 
 constexpr int kMinSliceUnits = 4;
+constexpr int kEpiNone = 0, kEpiSwiglu = 1, kEpiArgmax = 2;  // GemmPlan::epilogue
 constexpr int kFixupBatch = 8;  // split-K partials loaded together by the last workgroup
 
 constexpr int kRowPad = 8;          // fp16 pad per staged row (bank spread)
@@ -106,6 +107,23 @@ __device__ __forceinline__ h8 x_fragment(const _Float16* p) { return *reinterpre
 // silu(g) = g / (1 + e^-g) in fp32 (e^-g overflows to +inf for g < -88,
 // giving -0, the limit).
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// Greedy-argmax key of logit v at index n: the float's bits mapped to an
+// unsigned order (negative values flipped, positive ones above them) in the
+// high word and ~n in the low word, so the largest key is the largest logit
+// and, among equal logits, the smallest index. 0 means "nothing yet" (below
+// every real key, since -inf maps to 0x007FFFFF).
+__device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<unsigned long long>(ord) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(n));
+}
+
+__device__ __forceinline__ void argmax_decode(unsigned long long key, int* n, float* v) {
+  const uint32_t ord = static_cast<uint32_t>(key >> 32);
+  *n = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+  *v = __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
 
 // Sum over the S K ranges of one output's fp32 partials (stride apart), in
 // range order. The partials are fetched kFixupBatch at a time, all loads of a
@@ -152,17 +170,28 @@ __device__ __forceinline__ void unit_mfma(const Unit<kFmtFp8>& w, const _Float16
   }
 }
 
-template <int FMT, int WAVES, int DEPTH, bool SWIGLU>
+// Outputs of the greedy-argmax epilogue and its workspace.
+struct ArgmaxOut {
+  unsigned long long* keys;  // [groups][M]: each group's best key per row
+  int* done;                 // groups finished (the last one reduces the keys)
+  int* idx;                  // [M] int32 argmax
+  float* val;                // [M] fp32 max logit, or null
+};
+
+template <int FMT, int WAVES, int DEPTH, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     const _Float16* __restrict__ x, const uint8_t* packed,
     const float* __restrict__ row_scales, float tensor_scale, _Float16* __restrict__ y,
-    float* __restrict__ ws, int* __restrict__ counters, int M, int N, int K, int NT, int KU, int ups,
-    int stride, int KS) {
-  // SWIGLU (a template parameter, so the plain kernels carry none of it):
-  // output h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:], see the epilogues.
-  constexpr bool swiglu = SWIGLU;
+    float* __restrict__ ws, int* __restrict__ counters, ArgmaxOut amax, int M, int N, int K, int NT, int KU,
+    int ups, int stride, int KS) {
+  // The epilogue is a template parameter, so the plain kernels carry none of
+  // the others: kEpiSwiglu writes h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:],
+  // kEpiArgmax writes each row's largest logit and its index.
+  constexpr bool swiglu = EPI == kEpiSwiglu;
+  constexpr bool argmax = EPI == kEpiArgmax;
   extern __shared__ __align__(16) _Float16 xs[];
   __shared__ int last_group;
+  __shared__ unsigned long long best[kMaxM];
   constexpr int kBytes = Unit<FMT>::kBytes;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -312,6 +341,67 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     }
     return;
   }
+  // Greedy argmax: every row's best key over this group's logits (LDS
+  // atomics, order-free), stored for the group; the last group to finish
+  // reduces all groups' keys.
+  auto argmax_finish = [&]() {
+    __syncthreads();
+    if (tid < M)
+      __hip_atomic_store(amax.keys + static_cast<size_t>(blockIdx.x) * M + tid, best[tid], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int groups = gridDim.x;
+    if (tid == 0)
+      last_group = __hip_atomic_fetch_add(amax.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
+    if (tid < M) best[tid] = 0;
+    __syncthreads();
+    if (!last_group) return;
+    const int total = groups * M;
+    for (int i0 = tid; i0 < total; i0 += WAVES * 64 * kFixupBatch) {
+      unsigned long long part[kFixupBatch];
+#pragma unroll
+      for (int j = 0; j < kFixupBatch; ++j) {
+        const int i = i0 + j * WAVES * 64;
+        part[j] = i < total ? __hip_atomic_load(amax.keys + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      }
+#pragma unroll
+      for (int j = 0; j < kFixupBatch; ++j) {
+        const int i = i0 + j * WAVES * 64;
+        if (i < total) __hip_atomic_fetch_max(&best[i % M], part[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    __syncthreads();
+    if (tid < M) {
+      int n;
+      float v;
+      argmax_decode(best[tid], &n, &v);
+      amax.idx[tid] = n;
+      if (amax.val) amax.val[tid] = v;
+    }
+    if (tid == 0) __hip_atomic_store(amax.done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if (argmax) {
+    if (tid < M) best[tid] = 0;
+    __syncthreads();
+  }
+  if (S == 1 && argmax) {
+    if (owner && mcol < M) {
+      unsigned long long k = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = n0 + r;
+        if (n < N) {
+          const unsigned long long kr =
+              argmax_key(acc[r] * (FMT == kFmtNvfp4 ? tensor_scale : row_scales[n]), n);
+          k = kr > k ? kr : k;
+        }
+      }
+      __hip_atomic_fetch_max(&best[mcol], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    argmax_finish();
+    return;
+  }
   if (S == 1) {
     if (owner && mcol < M) {
       _Float16* dst = y + static_cast<size_t>(mcol) * N;
@@ -369,56 +459,73 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
       const float u = range_sum(src + Nh, range_stride, S) *
                       (FMT == kFmtNvfp4 ? tensor_scale : row_scales[n + Nh]);
       y[static_cast<size_t>(m) * Nh + n] = static_cast<_Float16>(silu(sum) * u);
+    } else if (argmax) {
+      __hip_atomic_fetch_max(&best[m], argmax_key(sum, n), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     } else {
       y[static_cast<size_t>(m) * N + n] = static_cast<_Float16>(sum);
     }
   }
   if (tid == 0) __hip_atomic_store(counters + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (argmax) argmax_finish();
 }
 
-template <int FMT, int WAVES, int DEPTH, bool SWIGLU>
+template <int FMT, int WAVES, int DEPTH, int EPI>
 hipError_t launch_cfg_e(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
-                      float tensor_scale, void* y, void* workspace, int m, int64_t n, int64_t k,
+                      float tensor_scale, void* y, float* val, void* workspace, int m, int64_t n, int64_t k,
                       hipStream_t stream) {
   const int NT = static_cast<int>(ceil_div(n, kTileN));
   const int KU = static_cast<int>(ceil_div(k, kUnitK));
   const unsigned groups = static_cast<unsigned>(ceil_div(NT, WAVES / p.k_slices));
   // Dynamic LDS above the 64 KiB default must be allowed per kernel.
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH, SWIGLU>),
+      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH, EPI>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBudget));
   if (attr != hipSuccess) return attr;
-  int* counters = p.split > 1 ? static_cast<int*>(workspace) : nullptr;
-  float* ws = p.split > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.partials_offset)
-                          : nullptr;
-  hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH, SWIGLU>), dim3(groups, static_cast<unsigned>(p.split)),
+  char* wsb = static_cast<char*>(workspace);
+  int* counters = p.split > 1 ? reinterpret_cast<int*>(wsb) : nullptr;
+  float* ws = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_offset) : nullptr;
+  ArgmaxOut amax{nullptr, nullptr, nullptr, nullptr};
+  if (EPI == kEpiArgmax) {
+    amax.keys = reinterpret_cast<unsigned long long*>(wsb + p.keys_offset);
+    amax.done = reinterpret_cast<int*>(wsb + p.control_offset);
+    amax.idx = static_cast<int*>(y);
+    amax.val = val;
+  }
+  hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH, EPI>), dim3(groups, static_cast<unsigned>(p.split)),
                      dim3(WAVES * 64), p.lds_bytes, stream, static_cast<const _Float16*>(x),
                      static_cast<const uint8_t*>(packed), row_scales, tensor_scale,
-                     static_cast<_Float16*>(y), ws, counters, m, static_cast<int>(n),
+                     static_cast<_Float16*>(y), ws, counters, amax, m, static_cast<int>(n),
                      static_cast<int>(k), NT, KU, p.units_per_split, p.lds_stride, p.k_slices);
   return hipGetLastError();
 }
 
 template <int FMT, int WAVES, int DEPTH>
 hipError_t launch_cfg(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
-                      float tensor_scale, void* y, void* workspace, int m, int64_t n, int64_t k,
+                      float tensor_scale, void* y, float* val, void* workspace, int m, int64_t n, int64_t k,
                       hipStream_t stream) {
-  return p.swiglu ? launch_cfg_e<FMT, WAVES, DEPTH, true>(p, x, packed, row_scales, tensor_scale, y, workspace,
-                                                          m, n, k, stream)
-                  : launch_cfg_e<FMT, WAVES, DEPTH, false>(p, x, packed, row_scales, tensor_scale, y, workspace,
-                                                           m, n, k, stream);
+  switch (p.epilogue) {
+    case kEpiSwiglu:
+      return launch_cfg_e<FMT, WAVES, DEPTH, kEpiSwiglu>(p, x, packed, row_scales, tensor_scale, y, val,
+                                                          workspace, m, n, k, stream);
+    case kEpiArgmax:
+      return launch_cfg_e<FMT, WAVES, DEPTH, kEpiArgmax>(p, x, packed, row_scales, tensor_scale, y, val,
+                                                          workspace, m, n, k, stream);
+    default:
+      return launch_cfg_e<FMT, WAVES, DEPTH, kEpiNone>(p, x, packed, row_scales, tensor_scale, y, val,
+                                                        workspace, m, n, k, stream);
+  }
 }
 
 template <int FMT, int WAVES>
 hipError_t launch_depth(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
-                        float tensor_scale, void* y, void* workspace, int m, int64_t n, int64_t k,
+                        float tensor_scale, void* y, float* val, void* workspace, int m, int64_t n, int64_t k,
                         hipStream_t stream) {
   switch (p.depth) {
-    case 2: return launch_cfg<FMT, WAVES, 2>(p, x, packed, row_scales, tensor_scale, y, workspace, m, n, k, stream);
-    case 3: return launch_cfg<FMT, WAVES, 3>(p, x, packed, row_scales, tensor_scale, y, workspace, m, n, k, stream);
-    case 6: return launch_cfg<FMT, WAVES, 6>(p, x, packed, row_scales, tensor_scale, y, workspace, m, n, k, stream);
-    case 8: return launch_cfg<FMT, WAVES, 8>(p, x, packed, row_scales, tensor_scale, y, workspace, m, n, k, stream);
-    default: return launch_cfg<FMT, WAVES, 4>(p, x, packed, row_scales, tensor_scale, y, workspace, m, n, k, stream);
+    case 2: return launch_cfg<FMT, WAVES, 2>(p, x, packed, row_scales, tensor_scale, y, val, workspace, m, n, k, stream);
+    case 3: return launch_cfg<FMT, WAVES, 3>(p, x, packed, row_scales, tensor_scale, y, val, workspace, m, n, k, stream);
+    case 6: return launch_cfg<FMT, WAVES, 6>(p, x, packed, row_scales, tensor_scale, y, val, workspace, m, n, k, stream);
+    case 8: return launch_cfg<FMT, WAVES, 8>(p, x, packed, row_scales, tensor_scale, y, val, workspace, m, n, k, stream);
+    default: return launch_cfg<FMT, WAVES, 4>(p, x, packed, row_scales, tensor_scale, y, val, workspace, m, n, k, stream);
   }
 }
 
@@ -470,7 +577,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   // needs an even number of n-tiles per workgroup (and N/2 on a tile
   // boundary): an automatic shape gives up K slices (or adds wavefronts) to
   // get there.
-  if (o.swiglu) {
+  if (o.epilogue == kEpiSwiglu) {
     if (n % (2 * kTileN)) return false;
     if (waves && ks && (waves / ks) % 2) {
       if (o.k_slices && o.waves) return false;
@@ -482,7 +589,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   if (waves != 4 && waves != 8) return false;
   if (ks != 1 && ks != 2 && ks != 4 && ks != 8) return false;
   if (ks > waves) return false;
-  if (o.swiglu && (waves / ks) % 2) return false;
+  if (o.epilogue == kEpiSwiglu && (waves / ks) % 2) return false;
   const int depth = w.depth ? w.depth : 3;
   if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
 
@@ -497,35 +604,38 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   const size_t red_bytes = ks > 1 ? static_cast<size_t>(waves) * 64 * sizeof(f4) : 0;
   if (p->lds_bytes < red_bytes) p->lds_bytes = red_bytes;
   // ... and (SwiGLU) the up tiles handed to the gate wavefronts.
-  const size_t xch_bytes = o.swiglu ? static_cast<size_t>(waves / ks / 2) * 64 * sizeof(f4) : 0;
+  const size_t xch_bytes = o.epilogue == kEpiSwiglu ? static_cast<size_t>(waves / ks / 2) * 64 * sizeof(f4) : 0;
   if (p->lds_bytes < xch_bytes) p->lds_bytes = xch_bytes;
-  p->swiglu = o.swiglu ? 1 : 0;
+  if (o.epilogue < kEpiNone || o.epilogue > kEpiArgmax) return false;
+  p->epilogue = o.epilogue;
+  const size_t counters = (static_cast<size_t>(NT) * sizeof(int) + 255) & ~size_t(255);
+  p->control_offset = counters;
+  p->partials_offset = counters + 256;
+  p->keys_offset = p->partials_offset;
+  p->workspace_bytes = 0;
   if (split > 1) {
-    // Counters first, one per n-tile (enough for any grouping of n-tiles),
-    // so that their place does not depend on m, split or workgroup shape and
-    // a workspace can be shared by calls with different row counts.
-    const size_t counters = static_cast<size_t>(NT) * sizeof(int);
-    p->partials_offset = (counters + 255) & ~size_t(255);
-    p->workspace_bytes = p->partials_offset + static_cast<size_t>(split) * m * n * sizeof(float);
-  } else {
-    p->partials_offset = 0;
-    p->workspace_bytes = 0;
+    p->keys_offset += (static_cast<size_t>(split) * m * n * sizeof(float) + 255) & ~size_t(255);
+    p->workspace_bytes = p->keys_offset;
+  }
+  if (o.epilogue == kEpiArgmax) {
+    const size_t groups = static_cast<size_t>(ceil_div(NT, waves / ks));
+    p->workspace_bytes = p->keys_offset + groups * m * sizeof(unsigned long long);
   }
   return true;
 }
 
 hipError_t launch_gemm(int fmt, const GemmPlan& p, const void* x, const void* packed,
-                       const float* row_scales, float tensor_scale, void* y, void* workspace,
+                       const float* row_scales, float tensor_scale, void* y, float* val, void* workspace,
                        int m, int64_t n, int64_t k, hipStream_t stream) {
   if (fmt == kFmtNvfp4) {
-    return p.waves == 8 ? launch_depth<kFmtNvfp4, 8>(p, x, packed, row_scales, tensor_scale, y,
+    return p.waves == 8 ? launch_depth<kFmtNvfp4, 8>(p, x, packed, row_scales, tensor_scale, y, val,
                                                       workspace, m, n, k, stream)
-                        : launch_depth<kFmtNvfp4, 4>(p, x, packed, row_scales, tensor_scale, y,
+                        : launch_depth<kFmtNvfp4, 4>(p, x, packed, row_scales, tensor_scale, y, val,
                                                       workspace, m, n, k, stream);
   }
-  return p.waves == 8 ? launch_depth<kFmtFp8, 8>(p, x, packed, row_scales, tensor_scale, y,
+  return p.waves == 8 ? launch_depth<kFmtFp8, 8>(p, x, packed, row_scales, tensor_scale, y, val,
                                                   workspace, m, n, k, stream)
-                      : launch_depth<kFmtFp8, 4>(p, x, packed, row_scales, tensor_scale, y,
+                      : launch_depth<kFmtFp8, 4>(p, x, packed, row_scales, tensor_scale, y, val,
                                                   workspace, m, n, k, stream);
 }
 

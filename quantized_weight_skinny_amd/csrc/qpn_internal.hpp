@@ -14,7 +14,7 @@ namespace qpn {
 // order.
 struct LaunchOverride {
   int split = 0, waves = 0, depth = 0, k_slices = 0;  // 0 = automatic
-  int swiglu = 0;  // 1: the SwiGLU epilogue (output h[M, N/2])
+  int epilogue = 0;  // 0: y[M, N]; 1: SwiGLU (h[M, N/2]); 2: greedy argmax per row
 };
 
 struct GemmPlan {
@@ -22,18 +22,27 @@ struct GemmPlan {
   int waves;
   int k_slices;    // wavefronts of a workgroup that split one n-tile's K range
   int depth;       // units of the weight stream each wavefront keeps in flight
-  int swiglu;      // epilogue: 0 y[M, N]; 1 h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:]
+  int epilogue;    // 0 y[M, N]; 1 h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:]; 2 argmax of each row
   int units_per_split;
   int lds_stride;  // halves per staged activation row
   size_t lds_bytes;
-  size_t partials_offset;  // the workspace holds per-group arrival counters, then
-  size_t workspace_bytes;  // fp32 partials [split][m][n] from this offset (0 if split == 1)
+  // Workspace: one split-K arrival counter per n-tile (padded to 256 bytes),
+  // a 256-byte control block (the argmax epilogue's counter), fp32 partials
+  // [split][m][n] from partials_offset (split > 1), then the argmax
+  // epilogue's per-group keys [groups][m] from keys_offset. 0 bytes when
+  // neither split-K nor the argmax epilogue needs it.
+  size_t control_offset;
+  size_t partials_offset;
+  size_t keys_offset;
+  size_t workspace_bytes;
 };
 
 bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, GemmPlan* plan);
 
+// y: fp16 output (or int32 indices for the argmax epilogue); val: the
+// argmax epilogue's fp32 max logits (may be null).
 hipError_t launch_gemm(int fmt, const GemmPlan& plan, const void* x, const void* packed,
-                       const float* row_scales, float tensor_scale, void* y, void* workspace,
+                       const float* row_scales, float tensor_scale, void* y, float* val, void* workspace,
                        int m, int64_t n, int64_t k, hipStream_t stream);
 
 hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,

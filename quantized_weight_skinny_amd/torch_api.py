@@ -8,6 +8,7 @@ returns the tensors it allocated. No arithmetic of the method happens here.
 import torch
 
 from . import (
+    QPN_EPILOGUE_ARGMAX,
     QPN_EPILOGUE_NONE,
     QPN_EPILOGUE_SWIGLU,
     QPN_ERR_BAD_CODE,
@@ -17,6 +18,7 @@ from . import (
     make_weight,
     qpn_absmax_f32,
     qpn_gemm,
+    qpn_gemm_argmax,
     qpn_gemm_tuned,
     qpn_nvfp4_tensor_scale,
     qpn_pack_fp8,
@@ -201,6 +203,31 @@ def gemm_swiglu(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_
     (zero shape fields: the shape qpn_gemm_swiglu uses)."""
     launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_SWIGLU)
     return _run(x, pw, out, workspace, launch, pw.n // 2)
+
+
+def argmax_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, device="cuda"):
+    """A zeroed workspace for gemm_argmax(pw) with up to m rows."""
+    launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_ARGMAX)
+    return torch.zeros(qpn_workspace_bytes_tuned(pw.desc(), m, launch), dtype=torch.uint8, device=device)
+
+
+def gemm_argmax(x, pw, idx=None, val=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0):
+    """(idx int32 [m], val fp32 [m]): each row's largest logit of
+    x @ dequant(W)^T and its index, through qpn_gemm_argmax."""
+    _cuda(x, torch.float16, "x")
+    m = x.shape[0]
+    launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_ARGMAX)
+    d = pw.desc()
+    need = qpn_workspace_bytes_tuned(d, m, launch)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    if idx is None:
+        idx = torch.empty(m, dtype=torch.int32, device=x.device)
+    if val is None:
+        val = torch.empty(m, dtype=torch.float32, device=x.device)
+    qpn_gemm_argmax(x.data_ptr(), d, idx.data_ptr(), val.data_ptr(), m, workspace.data_ptr(),
+                    workspace.numel() * workspace.element_size(), launch, _stream())
+    return idx, val
 
 
 def read_ceiling(buf, grid=0, sink=None):

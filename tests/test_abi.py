@@ -106,9 +106,10 @@ def test_gemm_workspace_checks():
     assert need > 0                                           # small N splits K
     assert _gemm(FAKE, w, FAKE, 8, None, 0) == q.QPN_ERR_INVALID_ARG
     assert _gemm(FAKE, w, FAKE, 8, FAKE, need - 16) == q.QPN_ERR_BUFFER_TOO_SMALL
-    # one counter per n-tile (padded to 256 bytes), then fp32 partials [split][m][n]
+    # one counter per n-tile (padded to 256 bytes), a 256-byte control block,
+    # then fp32 partials [split][m][n]
     counters = (5120 // 16) * 4
-    assert _ws(w, 8, split=5) == (counters + 255) // 256 * 256 + 5 * 8 * 5120 * 4
+    assert _ws(w, 8, split=5) == (counters + 255) // 256 * 256 + 256 + 5 * 8 * 5120 * 4
     # one K range of 17408 x 8 rows does not fit the activation stage in LDS
     assert _ws(w, 8, split=1) == 0
     assert _gemm(FAKE, w, FAKE, 8, FAKE, need, split=1) == q.QPN_ERR_UNSUPPORTED
@@ -160,6 +161,27 @@ def test_swiglu_epilogue_plans_and_checks():
     # unknown epilogue values are argument errors
     odd = q.make_launch(epilogue=2)
     assert q.lib().qpn_gemm_tuned(FAKE, ctypes.byref(_w()), FAKE, 1, None, 0, ctypes.byref(odd), None) == \
+        q.QPN_ERR_INVALID_ARG
+
+
+def test_argmax_epilogue_checks_and_workspace():
+    am = q.make_launch(epilogue=q.QPN_EPILOGUE_ARGMAX)
+    w = _w(n=151936, k=5120)
+    p = q.qpn_gemm_plan(w, 1, am)
+    assert p.epilogue == q.QPN_EPILOGUE_ARGMAX
+    groups = -(-(151936 // 16) // (p.waves_per_group // p.k_slices))
+    need = q.qpn_workspace_bytes_tuned(w, 1, am)
+    # counters, control block, then one 8-byte key per group and row
+    assert need == (151936 // 16 * 4 + 255) // 256 * 256 + 256 + groups * 8
+    idx, val = FAKE, FAKE + 64
+    call = q.lib().qpn_gemm_argmax
+    assert call(FAKE, ctypes.byref(w), idx, val, 1, None, 0, None, None) == q.QPN_ERR_INVALID_ARG
+    assert call(FAKE, ctypes.byref(w), idx, val, 1, FAKE, need - 8, None, None) == q.QPN_ERR_BUFFER_TOO_SMALL
+    assert call(FAKE, ctypes.byref(w), idx + 2, val, 1, FAKE, need, None, None) == q.QPN_ERR_INVALID_ARG
+    sw = q.make_launch(epilogue=q.QPN_EPILOGUE_SWIGLU)
+    assert call(FAKE, ctypes.byref(w), idx, val, 1, FAKE, need, ctypes.byref(sw), None) == q.QPN_ERR_INVALID_ARG
+    # the argmax epilogue has two outputs: not through qpn_gemm_tuned
+    assert q.lib().qpn_gemm_tuned(FAKE, ctypes.byref(w), FAKE, 1, FAKE, need, ctypes.byref(am), None) == \
         q.QPN_ERR_INVALID_ARG
 
 
