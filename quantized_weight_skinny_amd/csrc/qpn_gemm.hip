@@ -81,6 +81,10 @@ const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
 
 constexpr int kMinSliceUnits = 4;
 constexpr int kEpiNone = 0, kEpiSwiglu = 1, kEpiArgmax = 2;  // GemmPlan::epilogue
+// The argmax epilogue's arrival counters in the workspace's control block.
+constexpr int kArgmaxSubs = 64;
+constexpr int kCounterStride = 16;  // ints: one 64-byte line per counter
+constexpr size_t kControlBytes = (kArgmaxSubs + 1) * kCounterStride * sizeof(int) + 192;  // padded to 256
 constexpr int kFixupBatch = 8;  // split-K partials loaded together by the last workgroup
 
 constexpr int kRowPad = 8;          // fp16 pad per staged row (bank spread)
@@ -173,7 +177,7 @@ __device__ __forceinline__ void unit_mfma(const Unit<kFmtFp8>& w, const _Float16
 // Outputs of the greedy-argmax epilogue and its workspace.
 struct ArgmaxOut {
   unsigned long long* keys;  // [groups][M]: each group's best key per row
-  int* done;                 // groups finished (the last one reduces the keys)
+  int* done;                 // arrival counters: kArgmaxSubs, kCounterStride ints apart, then the total
   int* idx;                  // [M] int32 argmax
   float* val;                // [M] fp32 max logit, or null
 };
@@ -351,9 +355,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
                          __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // Arrival in two levels, so that thousands of groups do not queue on one
+    // counter: group g counts on sub-counter g % kArgmaxSubs (each on its own
+    // cache line); the last of each sub-counter's groups counts on the total.
     const int groups = gridDim.x;
-    if (tid == 0)
-      last_group = __hip_atomic_fetch_add(amax.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
+    if (tid == 0) {
+      const int sub = blockIdx.x % kArgmaxSubs;
+      const int members = (groups - 1 - sub) / kArgmaxSubs + 1;
+      int* sc = amax.done + sub * kCounterStride;
+      int last = __hip_atomic_fetch_add(sc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1;
+      if (last) {
+        __hip_atomic_store(sc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int* top = amax.done + kArgmaxSubs * kCounterStride;
+        const int subs = groups < kArgmaxSubs ? groups : kArgmaxSubs;
+        last = __hip_atomic_fetch_add(top, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == subs - 1;
+        if (last) __hip_atomic_store(top, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      last_group = last;
+    }
     if (tid < M) best[tid] = 0;
     __syncthreads();
     if (!last_group) return;
@@ -379,7 +398,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
       amax.idx[tid] = n;
       if (amax.val) amax.val[tid] = v;
     }
-    if (tid == 0) __hip_atomic_store(amax.done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   if (argmax) {
     if (tid < M) best[tid] = 0;
@@ -543,7 +561,18 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   if (max_ups < 1) return false;
 
   // A tuned launch for this shape fills in what the caller left automatic.
+  // The argmax epilogue ends every workgroup with a publication and a count,
+  // so it prefers few, wide groups: 8 n-tiles a workgroup, no K slices, depth
+  // 2 (measured on the 151936-row head: 72 us at M = 1 against 80 us with
+  // the plain GEMM's shape).
   LaunchOverride w = o;
+  if (o.epilogue == kEpiArgmax) {
+    if (!w.waves && !w.k_slices) {
+      w.waves = 8;
+      w.k_slices = 1;
+    }
+    if (!w.depth) w.depth = 2;
+  }
   if (const TunedLaunch* t = find_tuned(fmt, n, k, m)) {
     if (!w.split) w.split = t->split;
     if (!w.waves) w.waves = t->waves;
@@ -610,7 +639,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   p->epilogue = o.epilogue;
   const size_t counters = (static_cast<size_t>(NT) * sizeof(int) + 255) & ~size_t(255);
   p->control_offset = counters;
-  p->partials_offset = counters + 256;
+  p->partials_offset = counters + kControlBytes;
   p->keys_offset = p->partials_offset;
   p->workspace_bytes = 0;
   if (split > 1) {

@@ -27,7 +27,7 @@ struct GemmPlan {
   int lds_stride;  // halves per staged activation row
   size_t lds_bytes;
   // Workspace: one split-K arrival counter per n-tile (padded to 256 bytes),
-  // a 256-byte control block (the argmax epilogue's counter), fp32 partials
+  // a control block (the argmax epilogue's arrival counters), fp32 partials
   // [split][m][n] from partials_offset (split > 1), then the argmax
   // epilogue's per-group keys [groups][m] from keys_offset. 0 bytes when
   // neither split-K nor the argmax epilogue needs it.

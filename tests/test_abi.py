@@ -57,6 +57,10 @@ def test_tensor_scale_helper():
     assert q.qpn_nvfp4_tensor_scale(0.0) == 1.0
 
 
+# the workspace's control block: 64 + 1 arrival counters on 64-byte lines, padded
+CONTROL = 65 * 64 + 192
+
+
 def _w(fmt=q.QPN_FMT_NVFP4, n=512, k=1024, packed=FAKE, rs=FAKE):
     return q.make_weight(fmt, n, k, packed, 1.0, rs)
 
@@ -106,10 +110,10 @@ def test_gemm_workspace_checks():
     assert need > 0                                           # small N splits K
     assert _gemm(FAKE, w, FAKE, 8, None, 0) == q.QPN_ERR_INVALID_ARG
     assert _gemm(FAKE, w, FAKE, 8, FAKE, need - 16) == q.QPN_ERR_BUFFER_TOO_SMALL
-    # one counter per n-tile (padded to 256 bytes), a 256-byte control block,
-    # then fp32 partials [split][m][n]
+    # one counter per n-tile (padded to 256 bytes), the control block, then fp32
+    # partials [split][m][n]
     counters = (5120 // 16) * 4
-    assert _ws(w, 8, split=5) == (counters + 255) // 256 * 256 + 256 + 5 * 8 * 5120 * 4
+    assert _ws(w, 8, split=5) == (counters + 255) // 256 * 256 + CONTROL + 5 * 8 * 5120 * 4
     # one K range of 17408 x 8 rows does not fit the activation stage in LDS
     assert _ws(w, 8, split=1) == 0
     assert _gemm(FAKE, w, FAKE, 8, FAKE, need, split=1) == q.QPN_ERR_UNSUPPORTED
@@ -172,7 +176,7 @@ def test_argmax_epilogue_checks_and_workspace():
     groups = -(-(151936 // 16) // (p.waves_per_group // p.k_slices))
     need = q.qpn_workspace_bytes_tuned(w, 1, am)
     # counters, control block, then one 8-byte key per group and row
-    assert need == (151936 // 16 * 4 + 255) // 256 * 256 + 256 + groups * 8
+    assert need == (151936 // 16 * 4 + 255) // 256 * 256 + CONTROL + groups * 8
     idx, val = FAKE, FAKE + 64
     call = q.lib().qpn_gemm_argmax
     assert call(FAKE, ctypes.byref(w), idx, val, 1, None, 0, None, None) == q.QPN_ERR_INVALID_ARG

@@ -16,6 +16,8 @@ from quantized_weight_skinny_amd import torch_api as qt
 
 pytestmark = pytest.mark.gpu
 
+CONTROL = 65 * 64 + 192  # arrival counters of the workspace's control block
+
 
 def _check(idx, val, y_ref, b, what):
     cand = oracle.argmax_candidates(y_ref, b)
@@ -82,7 +84,7 @@ def test_argmax_equal_logits_take_the_smallest_index(fmt):
     for _ in range(3):
         idx, val = qt.gemm_argmax(to_dev(x), pw, workspace=ws)
         assert (to_host(idx) == 100).all()
-        assert not to_host(ws[:512]).any()       # 64 n-tile counters (256 B) and the control block
+        assert not to_host(ws[:256 + CONTROL]).any()   # 64 n-tile counters (256 B), control block
     y_ref, b = oracle_y(fmt, x, oracle_quantize(fmt, w))
     assert y_ref[0, 100] == y_ref[0].max()
 
@@ -101,7 +103,7 @@ def test_argmax_workspace_reuse_across_m_and_repeat():
         if m in ref:
             assert got == ref[m]
         ref[m] = got
-        assert not to_host(ws[:768]).any()       # 125 n-tile counters (512 B) and the control block
+        assert not to_host(ws[:512 + CONTROL]).any()   # 125 n-tile counters (512 B), control block
 
 
 def _lm_head_oracle(x, codes, scales, s_t, chunk=8192):
