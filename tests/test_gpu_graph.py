@@ -37,3 +37,43 @@ def test_graph_replay_matches_eager(fmt, n, k, m):
         assert np.array_equal(to_host(y).view(np.uint16), eager.view(np.uint16)), i
     if ws is not None:
         assert not to_host(ws[:64]).any()
+
+
+@pytest.mark.parametrize("split", [0, 3])
+def test_graph_replay_fused_epilogues(split):
+    """The SwiGLU and greedy-argmax epilogues captured together in one graph
+    (the argmax's arrival counters and the split-K counters are left at zero by
+    each call, so every replay reproduces the eager bits)."""
+    say("graph replay epilogues", split)
+    n, k, m = 2048, 2304, 5
+    w = workloads.weights(n, k, 41)
+    pw, _ = gpu_quantize("nvfp4", to_dev(w))
+    x = to_dev(workloads.activations(m, k, 42))
+    h = torch.empty((m, n // 2), dtype=torch.float16, device="cuda")
+    idx = torch.empty(m, dtype=torch.int32, device="cuda")
+    val = torch.empty(m, dtype=torch.float32, device="cuda")
+    kw = dict(split_k=split) if split else {}
+    ws_h = qt.new_workspace(pw, m, swiglu=True, **kw)
+    ws_a = qt.argmax_workspace(pw, m, **kw)
+
+    def run():
+        qt.gemm_swiglu(x, pw, out=h, workspace=ws_h, **kw)
+        qt.gemm_argmax(x, pw, idx=idx, val=val, workspace=ws_a, **kw)
+
+    run()
+    eager = (to_host(h).copy(), to_host(idx).copy(), to_host(val).copy())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(5):
+        h.fill_(0)
+        idx.fill_(-1)
+        val.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(h).view(np.uint16), eager[0].view(np.uint16)), i
+        assert np.array_equal(to_host(idx), eager[1]), i
+        assert np.array_equal(to_host(val).view(np.uint32), eager[2].view(np.uint32)), i
+    # 128 n-tile counters (512 B) and the control block are back at zero
+    assert not to_host(ws_a[:512 + 65 * 64 + 192]).any()
