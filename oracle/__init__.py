@@ -24,7 +24,8 @@ where wdq is the dequantized weight. The oracle writes that definition out in
 float64 (``gemm.py``), together with the format tables and encoders
 (``formats.py``), the quantizers that produce synthetic NVFP4 / FP8 weights
 (``quantize.py``), the canonical byte layout of packed codes (``layout.py``)
-and the SwiGLU that a fused gate_up epilogue computes (``mlp.py``).
+the SwiGLU that a fused gate_up epilogue computes (``mlp.py``) and the offline
+FP8 -> NVFP4 conversion (``requantize.py``).
 
 The pages never define the bit formats; the oracle uses the public
 definitions: E2M1 (OCP Microscaling spec v1.0, FP4 element type), E4M3 "FN"
@@ -62,6 +63,7 @@ from .gemm import (
     argmax_candidates,
 )
 from .mlp import silu, split_gate_up, swiglu, swiglu_tolerance
+from .requantize import dequantize_fp8_f32, requantize_fp8_to_nvfp4
 
 __all__ = [
     "E2M1_MAX", "E4M3_MAX", "e2m1_table", "e4m3_table", "decode_e2m1",
@@ -69,4 +71,5 @@ __all__ = [
     "quantize_fp8", "nvfp4_tensor_scale", "pack_nibbles", "unpack_nibbles",
     "dequantize_nvfp4", "dequantize_fp8", "skinny_gemm", "gemm_nvfp4",
     "gemm_fp8", "tolerance", "argmax_candidates", "silu", "split_gate_up", "swiglu", "swiglu_tolerance",
+    "dequantize_fp8_f32", "requantize_fp8_to_nvfp4",
 ]
