@@ -29,11 +29,11 @@ def test_requantize_hand_block():
     w = oracle.dequantize_fp8_f32(codes, rs)
     assert w[0, :8].tolist() == [0.5, 1.0, 1.5, 2.0, 0.25, 0.0, -0.5, 0.75]
     c, sc, s_t = oracle.requantize_fp8_to_nvfp4(codes, rs)
-    # amax 2.0: s_t = 2/2688; the block scale (2/6)/s_t = 448 -> E4M3 0x7E; d = fl(448 * s_t),
-    # just below 1/3, so w/d is just above 3 * w: 1.5, 3, 4.5 -> 4, 6, 0.75+ -> 1 (past the
-    # midpoint), 0, -1.5, 2.25 -> 2
+    # amax 2.0: s_t = 2/2688; the block scale (2/6)/s_t = 448 -> E4M3 0x7E; d = fl(448 * s_t)
+    # = fl(1/3), and w/d in fp32 is 3 * w: 1.5, 3, 4.5 -> 4, 6, 0.75 -> 1 (a tie: to the even
+    # code), 0, -1.5, 2.25 -> 2
     d = np.float32(np.float32(448.0) * np.float32(np.float32(2.0) / np.float32(2688.0)))
-    assert d < np.float32(1.0) / np.float32(3.0) or np.float32(0.25) / d > np.float32(0.75)
+    assert d == np.float32(1.0) / np.float32(3.0) and np.float32(0.25) / d == np.float32(0.75)
     assert s_t == np.float32(np.float32(2.0) / np.float32(2688.0))
     assert sc.tolist() == [[0x7E]]
     assert c[0, :8].tolist() == [0x3, 0x5, 0x6, 0x7, 0x2, 0x0, 0xB, 0x4]
