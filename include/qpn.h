@@ -141,6 +141,26 @@ qpn_status qpn_quantize_nvfp4(const float* w_dev, int64_t n, int64_t k, float te
 qpn_status qpn_quantize_fp8(const float* w_dev, int64_t n, int64_t k,
                             uint8_t* codes_dev, float* row_scales_dev, void* stream);
 
+/*
+ * Offline FP8 -> NVFP4 conversion ([P3] "v1.0 got us here. v1.1 removes its
+ * last compromise.": the first version served the checkpoint's FP8 regions
+ * by converting them to NVFP4). The FP8 weight (codes uint8 [n][k], no NaN
+ * codes; fp32 row scales [n]) stands for w = E4M3(c) * s_n, one fp32
+ * multiply per element; those values get the recipe of qpn_quantize_nvfp4.
+ *   qpn_fp8_absmax: out_dev[0] = max |w| (0 for an empty weight), for the
+ *     tensor scale qpn_nvfp4_tensor_scale(amax).
+ *   qpn_requantize_fp8_nvfp4: with that tensor scale (finite, > 0) ->
+ *     codes_dev uint8 [n][k/2] and block_scales_dev uint8 [n][k/16] as
+ *     qpn_quantize_nvfp4 writes them; pack with qpn_pack_nvfp4.
+ * k % 16 == 0. The conversion loses accuracy (E2M1 keeps 1 mantissa bit
+ * where E4M3 keeps 3), which is why the pages' second version kept FP8.
+ */
+qpn_status qpn_fp8_absmax(const uint8_t* codes_dev, const float* row_scales_dev, int64_t n, int64_t k,
+                          float* out_dev, void* stream);
+qpn_status qpn_requantize_fp8_nvfp4(const uint8_t* fp8_codes_dev, const float* row_scales_dev, int64_t n,
+                                    int64_t k, float tensor_scale, uint8_t* codes_dev, uint8_t* block_scales_dev,
+                                    void* stream);
+
 /* Device workspace qpn_gemm needs for this weight and row count (0 if none).
  * When K is split over several workgroups the workspace holds one arrival
  * counter per n-tile and fp32 partial sums. The counters sit at offsets that

@@ -82,6 +82,8 @@ SIGNATURES = {
     "qpn_nvfp4_tensor_scale": (_F, [_F]),
     "qpn_quantize_nvfp4": (_I32, [_P, _I64, _I64, _F, _P, _P, _P]),
     "qpn_quantize_fp8": (_I32, [_P, _I64, _I64, _P, _P, _P]),
+    "qpn_fp8_absmax": (_I32, [_P, _P, _I64, _I64, _P, _P]),
+    "qpn_requantize_fp8_nvfp4": (_I32, [_P, _P, _I64, _I64, _F, _P, _P, _P]),
     "qpn_workspace_bytes": (_SZ, [_W, _I32]),
     "qpn_workspace_bytes_tuned": (_SZ, [_W, _I32, _L]),
     "qpn_gemm_plan": (_I32, [_W, _I32, _L, _L]),
@@ -159,6 +161,15 @@ def qpn_quantize_nvfp4(w, n, k, tensor_scale, codes, block_scales, stream):
 
 def qpn_quantize_fp8(w, n, k, codes, row_scales, stream):
     return _check(lib().qpn_quantize_fp8(w, n, k, codes, row_scales, stream), "qpn_quantize_fp8")
+
+
+def qpn_fp8_absmax(codes, row_scales, n, k, out, stream):
+    return _check(lib().qpn_fp8_absmax(codes, row_scales, n, k, out, stream), "qpn_fp8_absmax")
+
+
+def qpn_requantize_fp8_nvfp4(fp8_codes, row_scales, n, k, tensor_scale, codes, block_scales, stream):
+    return _check(lib().qpn_requantize_fp8_nvfp4(fp8_codes, row_scales, n, k, tensor_scale, codes, block_scales,
+                                                 stream), "qpn_requantize_fp8_nvfp4")
 
 
 def make_weight(fmt, n, k, packed, tensor_scale=1.0, row_scales=None):

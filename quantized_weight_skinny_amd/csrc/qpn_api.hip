@@ -132,6 +132,25 @@ qpn_status qpn_quantize_fp8(const float* w_dev, int64_t n, int64_t k, uint8_t* c
   return from_hip(qpn::launch_quantize_fp8(w_dev, n, k, codes_dev, row_scales_dev, as_stream(stream)));
 }
 
+qpn_status qpn_fp8_absmax(const uint8_t* codes_dev, const float* row_scales_dev, int64_t n, int64_t k,
+                          float* out_dev, void* stream) {
+  if (!shape_ok(n, k) || !out_dev || !aligned(out_dev, 4)) return QPN_ERR_INVALID_ARG;
+  if (n > 0 && k > 0 && (!codes_dev || !row_scales_dev || !aligned(row_scales_dev, 4)))
+    return QPN_ERR_INVALID_ARG;
+  return from_hip(qpn::launch_fp8_absmax(codes_dev, row_scales_dev, n, k, out_dev, as_stream(stream)));
+}
+
+qpn_status qpn_requantize_fp8_nvfp4(const uint8_t* fp8_codes_dev, const float* row_scales_dev, int64_t n,
+                                    int64_t k, float tensor_scale, uint8_t* codes_dev, uint8_t* block_scales_dev,
+                                    void* stream) {
+  if (!shape_ok(n, k) || !isfinite(tensor_scale) || !(tensor_scale > 0.f)) return QPN_ERR_INVALID_ARG;
+  if (n == 0 || k == 0) return QPN_OK;
+  if (!fp8_codes_dev || !row_scales_dev || !codes_dev || !block_scales_dev || !aligned(row_scales_dev, 4))
+    return QPN_ERR_INVALID_ARG;
+  return from_hip(qpn::launch_requantize_fp8_nvfp4(fp8_codes_dev, row_scales_dev, n, k, tensor_scale, codes_dev,
+                                                   block_scales_dev, as_stream(stream)));
+}
+
 namespace {
 
 bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {

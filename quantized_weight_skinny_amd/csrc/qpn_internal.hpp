@@ -58,6 +58,10 @@ hipError_t launch_quantize_nvfp4(const float* w, int64_t n, int64_t k, float ten
                                  uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_quantize_fp8(const float* w, int64_t n, int64_t k, uint8_t* codes,
                                float* row_scales, hipStream_t stream);
+hipError_t launch_fp8_absmax(const uint8_t* codes, const float* row_scales, int64_t n, int64_t k, float* out,
+                             hipStream_t stream);
+hipError_t launch_requantize_fp8_nvfp4(const uint8_t* f8, const float* row_scales, int64_t n, int64_t k,
+                                       float tensor_scale, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, int grid,
                                hipStream_t stream);
 int read_ceiling_default_grid();

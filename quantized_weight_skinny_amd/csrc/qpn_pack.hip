@@ -171,6 +171,38 @@ __global__ __launch_bounds__(kBlock) void absmax_kernel(const float* __restrict_
   if ((threadIdx.x & 63) == 0 && m) atomicMax(out, m);
 }
 
+// The NVFP4 recipe for one 16-element block: its E4M3 scale (returned) and
+// 16 E2M1 codes, element i in nibble i of lo:hi.
+__device__ __forceinline__ uint32_t nvfp4_block(const float (&v)[16], float s_t, uint32_t& lo, uint32_t& hi) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t sc = encode_e4m3((amax / 6.0f) / s_t);
+  const float d = decode_e4m3(sc) * s_t;
+  lo = 0u;
+  hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t c = d == 0.f ? ((__float_as_uint(v[i]) >> 28) & 0x8u) : encode_e2m1(v[i] / d);
+    if (i < 8) lo |= c << (4 * i);
+    else hi |= c << (4 * (i - 8));
+  }
+  return sc;
+}
+
+__device__ __forceinline__ void store_nvfp4_block(uint8_t* codes, uint8_t* scales, int64_t K, int64_t n,
+                                                  int64_t b, int64_t idx, uint32_t lo, uint32_t hi,
+                                                  uint32_t sc) {
+  uint8_t* dst = codes + n * (K / 2) + b * 8;
+  if ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  } else {
+    for (int i = 0; i < 4; ++i) dst[i] = static_cast<uint8_t>(lo >> (8 * i));
+    for (int i = 0; i < 4; ++i) dst[4 + i] = static_cast<uint8_t>(hi >> (8 * i));
+  }
+  scales[idx] = static_cast<uint8_t>(sc);
+}
+
 // One thread per 16-element block of a row.
 __global__ __launch_bounds__(kBlock) void quantize_nvfp4_kernel(const float* __restrict__ w,
                                                                 int64_t N, int64_t K, float s_t,
@@ -184,26 +216,55 @@ __global__ __launch_bounds__(kBlock) void quantize_nvfp4_kernel(const float* __r
   float v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = src[i];
-  float amax = 0.f;
+  uint32_t lo, hi;
+  const uint32_t sc = nvfp4_block(v, s_t, lo, hi);
+  store_nvfp4_block(codes, scales, K, n, b, idx, lo, hi, sc);
+}
+
+// FP8 -> NVFP4 ([P3] "v1.0 got us here...": the first version converted the
+// checkpoint's FP8 regions to NVFP4). Each FP8 value is first the fp32 it
+// stands for, E4M3 value times the row scale (one rounding), then the block
+// is quantized as above.
+__global__ __launch_bounds__(kBlock) void requantize_fp8_nvfp4_kernel(const uint8_t* __restrict__ f8,
+                                                                      const float* __restrict__ row_scales,
+                                                                      int64_t N, int64_t K, float s_t,
+                                                                      uint8_t* __restrict__ codes,
+                                                                      uint8_t* __restrict__ scales) {
+  const int64_t nblk = K / 16;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (idx >= N * nblk) return;
+  const int64_t n = idx / nblk, b = idx - n * nblk;
+  const uint8_t* src = f8 + n * K + b * 16;
+  const float s_n = row_scales[n];
+  float v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const uint32_t sc = encode_e4m3((amax / 6.0f) / s_t);
-  const float d = decode_e4m3(sc) * s_t;
-  uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t c = d == 0.f ? ((__float_as_uint(v[i]) >> 28) & 0x8u) : encode_e2m1(v[i] / d);
-    if (i < 8) lo |= c << (4 * i);
-    else hi |= c << (4 * (i - 8));
+  for (int i = 0; i < 16; ++i) v[i] = decode_e4m3(src[i]) * s_n;
+  uint32_t lo, hi;
+  const uint32_t sc = nvfp4_block(v, s_t, lo, hi);
+  store_nvfp4_block(codes, scales, K, n, b, idx, lo, hi, sc);
+}
+
+// max |E4M3(c) * s_n| over an FP8 weight: per row the largest code
+// magnitude (the E4M3 order is the order of its magnitude bits), decoded and
+// scaled, as fp32 bits for the integer max. One workgroup per row.
+__global__ __launch_bounds__(kBlock) void fp8_absmax_kernel(const uint8_t* __restrict__ f8,
+                                                            const float* __restrict__ row_scales, int64_t K,
+                                                            uint32_t* __restrict__ out) {
+  const int64_t n = blockIdx.x;
+  const uint8_t* src = f8 + n * K;
+  uint32_t m = 0u;
+  for (int64_t i = threadIdx.x; i < K; i += kBlock) {
+    const uint32_t c = src[i] & 0x7Fu;
+    m = c > m ? c : m;
   }
-  uint8_t* dst = codes + n * (K / 2) + b * 8;
-  if ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-  } else {
-    for (int i = 0; i < 4; ++i) dst[i] = static_cast<uint8_t>(lo >> (8 * i));
-    for (int i = 0; i < 4; ++i) dst[4 + i] = static_cast<uint8_t>(hi >> (8 * i));
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, 64));
+    m = o > m ? o : m;
   }
-  scales[idx] = static_cast<uint8_t>(sc);
+  if ((threadIdx.x & 63) == 0 && m) {
+    const uint32_t b = __float_as_uint(fabsf(decode_e4m3(m) * row_scales[n]));
+    if (b) atomicMax(out, b);
+  }
 }
 
 // One workgroup per row: row absmax, then the codes.
@@ -315,6 +376,25 @@ hipError_t launch_quantize_nvfp4(const float* w, int64_t n, int64_t k, float ten
   if (t == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_nvfp4_kernel, dim3(blocks_for(t)), dim3(kBlock), 0, stream, w, n, k,
                      tensor_scale, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_absmax(const uint8_t* codes, const float* row_scales, int64_t n, int64_t k, float* out,
+                             hipStream_t stream) {
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  hipLaunchKernelGGL(absmax_init, dim3(1), dim3(1), 0, stream, o);
+  if (n > 0 && k > 0)
+    hipLaunchKernelGGL(fp8_absmax_kernel, dim3(static_cast<unsigned>(n)), dim3(kBlock), 0, stream, codes,
+                       row_scales, k, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_requantize_fp8_nvfp4(const uint8_t* f8, const float* row_scales, int64_t n, int64_t k,
+                                       float tensor_scale, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const int64_t t = n * (k / 16);
+  if (t == 0) return hipSuccess;
+  hipLaunchKernelGGL(requantize_fp8_nvfp4_kernel, dim3(blocks_for(t)), dim3(kBlock), 0, stream, f8, row_scales,
+                     n, k, tensor_scale, codes, scales);
   return hipGetLastError();
 }
 

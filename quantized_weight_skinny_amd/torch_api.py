@@ -17,6 +17,8 @@ from . import (
     QpnError,
     make_weight,
     qpn_absmax_f32,
+    qpn_fp8_absmax,
+    qpn_requantize_fp8_nvfp4,
     qpn_gemm,
     qpn_gemm_argmax,
     qpn_gemm_tuned,
@@ -151,6 +153,23 @@ def quantize_fp8(w):
     rs = torch.empty(n, dtype=torch.float32, device=w.device)
     qpn_quantize_fp8(w.data_ptr(), n, k, codes.data_ptr(), rs.data_ptr(), _stream())
     return codes, rs
+
+
+def requantize_fp8_to_nvfp4(codes8, row_scales):
+    """(codes [n, k/2], block scales [n, k/16], tensor scale) of an FP8 weight
+    (uint8 codes [n, k], fp32 row scales [n]) converted to NVFP4 on the GPU;
+    pack the result with pack_nvfp4."""
+    _cuda(codes8, torch.uint8, "codes")
+    _cuda(row_scales, torch.float32, "row_scales")
+    n, k = codes8.shape
+    amax = torch.empty(1, dtype=torch.float32, device=codes8.device)
+    qpn_fp8_absmax(codes8.data_ptr(), row_scales.data_ptr(), n, k, amax.data_ptr(), _stream())
+    s_t = qpn_nvfp4_tensor_scale(float(amax.item()))
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=codes8.device)
+    scales = torch.empty((n, k // 16), dtype=torch.uint8, device=codes8.device)
+    qpn_requantize_fp8_nvfp4(codes8.data_ptr(), row_scales.data_ptr(), n, k, s_t, codes.data_ptr(),
+                             scales.data_ptr(), _stream())
+    return codes, scales, s_t
 
 
 def _launch(split_k=0, waves=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE):

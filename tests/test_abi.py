@@ -189,6 +189,18 @@ def test_argmax_epilogue_checks_and_workspace():
         q.QPN_ERR_INVALID_ARG
 
 
+def test_requantize_rejects_bad_arguments():
+    L = q.lib()
+    err = q.QPN_ERR_INVALID_ARG
+    assert L.qpn_requantize_fp8_nvfp4(FAKE, FAKE, 4, 32, 0.0, FAKE, FAKE, None) == err      # scale 0
+    assert L.qpn_requantize_fp8_nvfp4(FAKE, FAKE, 4, 32, float("inf"), FAKE, FAKE, None) == err
+    assert L.qpn_requantize_fp8_nvfp4(FAKE, FAKE, 4, 40, 1.0, FAKE, FAKE, None) == err      # k % 16
+    assert L.qpn_requantize_fp8_nvfp4(None, FAKE, 4, 32, 1.0, FAKE, FAKE, None) == err
+    assert L.qpn_requantize_fp8_nvfp4(FAKE, FAKE, 0, 32, 1.0, None, None, None) == q.QPN_OK  # empty
+    assert L.qpn_fp8_absmax(FAKE, FAKE, 4, 32, None, None) == err
+    assert L.qpn_fp8_absmax(FAKE, FAKE + 2, 4, 32, FAKE, None) == err                        # misaligned
+
+
 def test_pack_and_quantize_reject_bad_arguments():
     lib = q.lib()
     nv = q.qpn_packed_bytes(q.QPN_FMT_NVFP4, 32, 64)
