@@ -200,9 +200,21 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *                    their results through LDS;
  *   epilogue         QPN_EPILOGUE_NONE (y as in qpn_gemm), QPN_EPILOGUE_SWIGLU
  *                    (see qpn_gemm_swiglu) or QPN_EPILOGUE_ARGMAX (only with
- *                    qpn_gemm_argmax and the workspace / plan queries).
+ *                    qpn_gemm_argmax and the workspace / plan queries);
+ *   x_stage          how the activation rows reach LDS (0 = automatic):
+ *                    QPN_X_STAGE_FULL copies the workgroup's whole K range
+ *                    before the weight stream starts (one barrier; LDS of
+ *                    2 * m * range bytes, so a long K at large m must be
+ *                    split); QPN_X_STAGE_RING keeps three 256-element units
+ *                    per K slice in a ring refilled one unit ahead of the
+ *                    stream (one barrier per unit; LDS of
+ *                    1584 * m * k_slices bytes; needs depth 2..4,
+ *                    k_slices * m <= 4 * waves_per_group and 2 * m * k < 2^31).
+ * The result bits depend on split_k and k_slices (the summation order), not
+ * on the other fields.
  */
 typedef enum { QPN_EPILOGUE_NONE = 0, QPN_EPILOGUE_SWIGLU = 1, QPN_EPILOGUE_ARGMAX = 2 } qpn_epilogue;
+typedef enum { QPN_X_STAGE_AUTO = 0, QPN_X_STAGE_FULL = 1, QPN_X_STAGE_RING = 2 } qpn_x_stage;
 
 typedef struct {
   int32_t split_k;
@@ -210,11 +222,13 @@ typedef struct {
   int32_t depth;
   int32_t k_slices;
   int32_t epilogue;
-  int32_t reserved[3]; /* must be 0 */
+  int32_t x_stage;
+  int32_t reserved[2]; /* must be 0 */
 } qpn_launch;
 
-/* qpn_gemm with an explicit launch shape (NULL = automatic). A shape whose
- * activation stage does not fit in LDS returns QPN_ERR_UNSUPPORTED. */
+/* qpn_gemm with an explicit launch shape (NULL = automatic). A shape that
+ * is not possible (an activation stage that does not fit in LDS, a ring
+ * outside its limits) returns QPN_ERR_UNSUPPORTED. */
 qpn_status qpn_gemm_tuned(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
                           void* workspace_dev, size_t workspace_bytes,
                           const qpn_launch* launch, void* stream);

@@ -31,6 +31,9 @@ QPN_MAX_M = 16
 QPN_EPILOGUE_NONE = 0
 QPN_EPILOGUE_SWIGLU = 1
 QPN_EPILOGUE_ARGMAX = 2
+QPN_X_STAGE_AUTO = 0
+QPN_X_STAGE_FULL = 1
+QPN_X_STAGE_RING = 2
 
 
 class QpnError(RuntimeError):
@@ -46,7 +49,8 @@ class qpn_launch(ctypes.Structure):
         ("depth", ctypes.c_int32),
         ("k_slices", ctypes.c_int32),
         ("epilogue", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("x_stage", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -180,8 +184,9 @@ def qpn_workspace_bytes(weight, m):
     return lib().qpn_workspace_bytes(ctypes.byref(weight), m)
 
 
-def make_launch(split_k=0, waves_per_group=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE):
-    return qpn_launch(split_k, waves_per_group, depth, k_slices, epilogue)
+def make_launch(split_k=0, waves_per_group=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE,
+                x_stage=QPN_X_STAGE_AUTO):
+    return qpn_launch(split_k, waves_per_group, depth, k_slices, epilogue, x_stage)
 
 
 def qpn_workspace_bytes_tuned(weight, m, launch):

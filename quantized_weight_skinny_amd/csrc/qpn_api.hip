@@ -155,8 +155,10 @@ namespace {
 
 bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   if (!l) return true;
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < 2; ++i)
     if (l->reserved[i] != 0) return false;
+  if (l->x_stage != QPN_X_STAGE_AUTO && l->x_stage != QPN_X_STAGE_FULL && l->x_stage != QPN_X_STAGE_RING)
+    return false;
   if (l->split_k < 0 || l->waves_per_group < 0 || l->depth < 0 || l->k_slices < 0) return false;
   if (l->epilogue != QPN_EPILOGUE_NONE && l->epilogue != QPN_EPILOGUE_SWIGLU && l->epilogue != QPN_EPILOGUE_ARGMAX)
     return false;
@@ -165,6 +167,7 @@ bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   o->depth = l->depth;
   o->k_slices = l->k_slices;
   o->epilogue = l->epilogue;
+  o->x_stage = l->x_stage;
   return true;
 }
 
@@ -196,6 +199,7 @@ qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launc
   resolved->depth = p.depth;
   resolved->k_slices = p.k_slices;
   resolved->epilogue = p.epilogue;
+  resolved->x_stage = p.x_stage;
   return QPN_OK;
 }
 

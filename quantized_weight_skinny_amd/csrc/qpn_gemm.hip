@@ -15,9 +15,12 @@
 // design becomes the 16-row MFMA tile here).
 //
 // Work split: each wavefront owns one 16-row n-tile and a contiguous range of
-// 256-element K units. A workgroup holds `WAVES` neighbouring n-tiles of the
-// same K range and first stages x[:, range] into LDS (one 16-byte
-// ds_read_b128 per lane per MFMA later). Loads of DEPTH units are kept in
+// 256-element K units. A workgroup holds neighbouring n-tiles of the same K
+// range (cut into K slices, one per wavefront of a tile) and stages x into
+// LDS, read back as one 16-byte ds_read_b128 per lane per MFMA: either the
+// whole range before the weight stream starts, or a ring of three units per
+// slice refilled alongside the stream (a much smaller stage, so that large M
+// keeps its occupancy and needs no K split). Loads of DEPTH units are kept in
 // flight per wavefront. When K is cut into several ranges the fp32 partial
 // tiles go to a workspace and the last workgroup of each group of n-tiles to
 // finish adds them in range order, which keeps the result deterministic and
@@ -32,9 +35,10 @@ namespace {
 // few bytes of static LDS) fit the 160 KiB of LDS in a CU.
 constexpr size_t kLdsBudget = 79 * 1024;
 // Launch shapes. For the matrices of a ~27B dense decoder (hidden 5120) the
-// launch comes from a table measured on MI355X: a sweep of workgroup size x
-// K slices x K split x stream depth, best graph-replayed time per launch at
-// M = 1, 2, 4, 8. Other shapes use a rule distilled from the same sweep:
+// launch comes from a table measured on MI355X: a sweep of activation stage x
+// workgroup size x K slices x K split x stream depth, best graph-replayed time
+// per launch at M = 1, 2, 4, 8, 16. Other shapes use a rule distilled from the
+// same sweep:
 //  * a workgroup holds TN n-tiles that share one staged copy of x (the
 //    staging reads 2*M bytes of x per K element against 9*TN bytes of NVFP4
 //    weights), TN = 2 up to M = 4 and 4 above;
@@ -42,35 +46,42 @@ constexpr size_t kLdsBudget = 79 * 1024;
 //    K slices, reduced through LDS, keeping >= kMinSliceUnits units a slice;
 //  * K is split over workgroups only as far as the activation stage must be
 //    cut to fit LDS (that reduction costs memory round trips at the tail);
-//  * a stream depth of 3 units.
+//  * a stream depth of 3 units;
+//  * the ring activation stage from kRingMinM rows on (at 8 and 16 rows it
+//    wins on every matrix but one, at 4 it ties with the full stage).
 struct TunedLaunch {
   int fmt;
   int64_t n, k;
   int m_max;  // entry applies to m <= m_max (entries of a shape in increasing m_max)
   int waves, k_slices, split, depth;
+  int x_stage = kStageFull;
 };
 
 constexpr TunedLaunch kTuned[] = {
     // NVFP4 gate_up 34816 x 5120
     {kFmtNvfp4, 34816, 5120, 1, 4, 4, 1, 3}, {kFmtNvfp4, 34816, 5120, 2, 4, 4, 1, 2},
-    {kFmtNvfp4, 34816, 5120, 4, 8, 4, 1, 2}, {kFmtNvfp4, 34816, 5120, 8, 8, 2, 2, 2},
+    {kFmtNvfp4, 34816, 5120, 4, 8, 4, 1, 2}, {kFmtNvfp4, 34816, 5120, 8, 4, 2, 1, 2, kStageRing},
+    {kFmtNvfp4, 34816, 5120, 16, 8, 2, 1, 2, kStageRing},
     // NVFP4 down 5120 x 17408
     {kFmtNvfp4, 5120, 17408, 2, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 17408, 4, 8, 2, 3, 2},
-    {kFmtNvfp4, 5120, 17408, 8, 8, 2, 6, 2},
+    {kFmtNvfp4, 5120, 17408, 8, 8, 2, 3, 2, kStageRing}, {kFmtNvfp4, 5120, 17408, 16, 8, 2, 3, 2, kStageRing},
     // NVFP4 qkv 7168 x 5120 and o_proj 5120 x 5120
-    {kFmtNvfp4, 7168, 5120, 4, 8, 4, 1, 3}, {kFmtNvfp4, 7168, 5120, 8, 8, 2, 2, 2},
-    {kFmtNvfp4, 5120, 5120, 4, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 5120, 8, 8, 2, 3, 2},
+    {kFmtNvfp4, 7168, 5120, 4, 8, 4, 1, 3}, {kFmtNvfp4, 7168, 5120, 8, 8, 4, 1, 2, kStageRing},
+    {kFmtNvfp4, 7168, 5120, 16, 8, 2, 2, 2, kStageRing},
+    {kFmtNvfp4, 5120, 5120, 4, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 5120, 8, 8, 4, 1, 2, kStageRing},
+    {kFmtNvfp4, 5120, 5120, 16, 8, 2, 3, 2},
     // NVFP4 lm_head 151936 x 5120
-    {kFmtNvfp4, 151936, 5120, 1, 8, 4, 1, 3}, {kFmtNvfp4, 151936, 5120, 2, 4, 2, 1, 2},
-    {kFmtNvfp4, 151936, 5120, 4, 8, 2, 1, 2}, {kFmtNvfp4, 151936, 5120, 8, 8, 1, 2, 2},
+    {kFmtNvfp4, 151936, 5120, 1, 8, 4, 1, 3}, {kFmtNvfp4, 151936, 5120, 2, 4, 2, 1, 2, kStageRing},
+    {kFmtNvfp4, 151936, 5120, 4, 8, 2, 1, 2}, {kFmtNvfp4, 151936, 5120, 16, 8, 1, 1, 2, kStageRing},
     // FP8 qkv 7168 x 5120
-    {kFmtFp8, 7168, 5120, 4, 4, 2, 1, 2}, {kFmtFp8, 7168, 5120, 8, 8, 2, 2, 2},
+    {kFmtFp8, 7168, 5120, 2, 4, 2, 1, 2}, {kFmtFp8, 7168, 5120, 4, 4, 2, 1, 3, kStageRing},
+    {kFmtFp8, 7168, 5120, 8, 4, 2, 1, 2, kStageRing}, {kFmtFp8, 7168, 5120, 16, 8, 2, 2, 2, kStageRing},
     // FP8 o_proj 5120 x 5120
-    {kFmtFp8, 5120, 5120, 2, 4, 2, 1, 3}, {kFmtFp8, 5120, 5120, 4, 8, 4, 1, 2},
-    {kFmtFp8, 5120, 5120, 8, 8, 2, 3, 2},
+    {kFmtFp8, 5120, 5120, 1, 4, 2, 1, 3}, {kFmtFp8, 5120, 5120, 2, 4, 2, 1, 4},
+    {kFmtFp8, 5120, 5120, 8, 4, 2, 1, 3, kStageRing}, {kFmtFp8, 5120, 5120, 16, 8, 2, 3, 2, kStageRing},
     // FP8 down 5120 x 17408
-    {kFmtFp8, 5120, 17408, 2, 8, 4, 1, 2}, {kFmtFp8, 5120, 17408, 4, 8, 2, 3, 3},
-    {kFmtFp8, 5120, 17408, 8, 8, 2, 6, 2},
+    {kFmtFp8, 5120, 17408, 1, 8, 4, 1, 2}, {kFmtFp8, 5120, 17408, 4, 4, 1, 3, 3, kStageRing},
+    {kFmtFp8, 5120, 17408, 16, 8, 2, 3, 3, kStageRing},
 };
 
 const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
@@ -80,6 +91,7 @@ const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
 }
 
 constexpr int kMinSliceUnits = 4;
+constexpr int kRingMinM = 5;
 constexpr int kEpiNone = 0, kEpiSwiglu = 1, kEpiArgmax = 2;  // GemmPlan::epilogue
 // The argmax epilogue's arrival counters in the workspace's control block.
 constexpr int kArgmaxSubs = 64;
@@ -88,6 +100,9 @@ constexpr size_t kControlBytes = (kArgmaxSubs + 1) * kCounterStride * sizeof(int
 constexpr int kFixupBatch = 8;  // split-K partials loaded together by the last workgroup
 
 constexpr int kRowPad = 8;          // fp16 pad per staged row (bank spread)
+constexpr int kRingSlots = 3;       // units per K slice in the ring stage
+constexpr int kRingRow = kUnitK + kRowPad;  // halves per row of a ring slot
+constexpr int kRingMaxPieces = 2;   // x pieces per thread and unit in the ring stage
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -182,9 +197,10 @@ struct ArgmaxOut {
   float* val;                // [M] fp32 max logit, or null
 };
 
-template <int FMT, int WAVES, int DEPTH, int EPI>
+// XP = 0: full stage; XP > 0: ring stage with XP x pieces per thread.
+template <int FMT, int WAVES, int DEPTH, int EPI, int XP>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
-    const _Float16* __restrict__ x, const uint8_t* packed,
+    const _Float16* x, const uint8_t* packed,
     const float* __restrict__ row_scales, float tensor_scale, _Float16* __restrict__ y,
     float* __restrict__ ws, int* __restrict__ counters, ArgmaxOut amax, int M, int N, int K, int NT, int KU,
     int ups, int stride, int KS) {
@@ -225,79 +241,158 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
                       active && wnu > 0 ? static_cast<uint32_t>(wnu - 1) * unit_stride + kBytes : 0u,
                       unit_stride);
 
-  // Stage this K range of every activation row in LDS with direct-to-LDS
-  // loads: one global_load_lds_dwordx4 moves 64 lanes x 16 B (two units of
-  // one row) without passing through registers, so all of them can be in
-  // flight at once. Chunks past K (the zero-padded tail of the last unit)
-  // are written as zeros first, so that 0 * x stays finite; lanes past the
-  // row's staged length are masked off.
-  const int row_chunks = nu * (kUnitK / 8);
-  const int kbase = u0 * kUnitK;
-  const int live_chunks = min(row_chunks, max(0, (K - kbase) / 8));
-  if (live_chunks < row_chunks) {
-    const int tail = row_chunks - live_chunks;
-    for (int idx = tid; idx < M * tail; idx += WAVES * 64) {
-      const int m = idx / tail;
-      *reinterpret_cast<uint4*>(xs + m * stride + (live_chunks + idx - m * tail) * 8) =
-          make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  const int windows = (live_chunks + 63) / 64;
-  for (int wi = wave; wi < M * windows; wi += WAVES) {
-    const int m = wi / windows;
-    const int c0 = (wi - m * windows) * 64;
-    if (c0 + lane < live_chunks)
-      lds_dma16(x + static_cast<size_t>(m) * K + kbase + (c0 + lane) * 8, xs + m * stride + c0 * 8);
-  }
-
-  // Then issue the first DEPTH units of the weight stream unit by unit, in
-  // the order the loop will consume them. (`packed` is deliberately not
-  // __restrict__: with it the compiler may treat the weights as immutable and
-  // sink these loads past the barrier below, which would both delay the
-  // stream and break the staging wait.) Loads are never conditional: a
-  // unit past the wavefront's range lies past the stream's byte range, so
-  // the buffer load returns zeros without touching memory. This keeps the
-  // compiler's view of in-flight loads exact at every point.
-  Unit<FMT> buf[DEPTH];
-#pragma unroll
-  for (int i = 0; i < DEPTH; ++i) {
-    load_unit(buf[i], stream, i, lane);
-    asm volatile("" ::: "memory");  // keep the units' loads in this order
-  }
-  // Wait for the staging loads only (they were issued before the weight
-  // loads, and the counter retires loads in order) and for the zero stores,
-  // then meet at a bare barrier: the weight loads stay in flight across it.
-  // (A full __syncthreads would also wait for them.)
-  __builtin_amdgcn_s_waitcnt(vmcnt_only(Unit<FMT>::kLoads * DEPTH));
-  __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-
   // B-operand column m of the MFMA is activation row m. Lanes of columns
   // m >= M read row M-1 (an LDS broadcast); their output columns are never
   // stored, and MFMA output columns do not mix, so they need no zeroing.
   const int mcol = lane & 15;
   const int g = lane >> 4;
-  const _Float16* xrow = xs + min(mcol, M - 1) * stride + g * 64 + wu0 * kUnitK;
   f4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // Loads of the weight stream are never conditional: a unit past the
+  // wavefront's range lies past the stream's byte range, so the buffer load
+  // returns zeros without touching memory. This keeps the compiler's view of
+  // in-flight loads exact at every point. (`packed` is deliberately not
+  // __restrict__: with it the compiler may treat the weights as immutable
+  // and move their loads across the staging barriers, which would both delay
+  // the stream and break the staging waits.)
+  Unit<FMT> buf[DEPTH];
 
-  if (active) {
-    // Each slot of buf is consumed and then refilled in place (unit u + DEPTH
-    // goes where unit u was), so the loop carries no register copies and
-    // keeps DEPTH-1 units in flight while it computes. Refills past the end
-    // of the range read zeros and cost no memory traffic.
-    for (int base = 0; base < wnu; base += DEPTH) {
+  if constexpr (XP == 0) {
+    // Full stage: this K range of every activation row goes to LDS before
+    // the stream starts, with direct-to-LDS loads: one
+    // global_load_lds_dwordx4 moves 64 lanes x 16 B (two units of one row)
+    // without passing through registers, so all of them can be in flight at
+    // once. Chunks past K (the zero-padded tail of the last unit) are
+    // written as zeros first, so that 0 * x stays finite; lanes past the
+    // row's staged length are masked off.
+    const int row_chunks = nu * (kUnitK / 8);
+    const int kbase = u0 * kUnitK;
+    const int live_chunks = min(row_chunks, max(0, (K - kbase) / 8));
+    if (live_chunks < row_chunks) {
+      const int tail = row_chunks - live_chunks;
+      for (int idx = tid; idx < M * tail; idx += WAVES * 64) {
+        const int m = idx / tail;
+        *reinterpret_cast<uint4*>(xs + m * stride + (live_chunks + idx - m * tail) * 8) =
+            make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    const int windows = (live_chunks + 63) / 64;
+    for (int wi = wave; wi < M * windows; wi += WAVES) {
+      const int m = wi / windows;
+      const int c0 = (wi - m * windows) * 64;
+      if (c0 + lane < live_chunks)
+        lds_dma16(x + static_cast<size_t>(m) * K + kbase + (c0 + lane) * 8, xs + m * stride + c0 * 8);
+    }
+
+    // Then issue the first DEPTH units of the weight stream unit by unit, in
+    // the order the loop will consume them.
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+      load_unit(buf[i], stream, i, lane);
+      asm volatile("" ::: "memory");  // keep the units' loads in this order
+    }
+    // Wait for the staging loads only (they were issued before the weight
+    // loads, and the counter retires loads in order) and for the zero
+    // stores, then meet at a bare barrier: the weight loads stay in flight
+    // across it. (A full __syncthreads would also wait for them.)
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(Unit<FMT>::kLoads * DEPTH));
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    const _Float16* xrow = xs + min(mcol, M - 1) * stride + g * 64 + wu0 * kUnitK;
+    if (active) {
+      // Each slot of buf is consumed and then refilled in place (unit u +
+      // DEPTH goes where unit u was), so the loop carries no register copies
+      // and keeps DEPTH-1 units in flight while it computes.
+      for (int base = 0; base < wnu; base += DEPTH) {
+#pragma unroll
+        for (int i = 0; i < DEPTH; ++i) {
+          if (base + i < wnu) unit_mfma(buf[i], xrow + (base + i) * kUnitK, acc2);
+          load_unit(buf[i], stream, base + DEPTH + i, lane);
+          // keep the scheduler from sinking the refill below the next units' math
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  } else {
+    // Ring stage: each K slice keeps the activations of three units in LDS
+    // (slot c % 3 holds unit c of the slice, all M rows), and the workgroup
+    // refills one slot per unit of the stream. The x pieces (8 halves of one
+    // row) of a unit are loaded into registers DEPTH + 1 units ahead,
+    // alongside the weights, and written to LDS one unit ahead; a barrier
+    // per unit publishes the slot. Three slots suffice: the slot written at
+    // step j was last read at step j - 2, which every wavefront has finished
+    // once it has passed the barrier of step j - 1. The stage is
+    // 3 * KS * M * 528 bytes whatever K is, so long K ranges need no split.
+    const int slot_halves = M * kRingRow;
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<_Float16*>(x), 0, static_cast<uint32_t>(M) * K * 2, Stream::kRsrcWord3);
+    // Piece p of a step: slice p / (32 M), row (p / 32) % M, 8 halves at q * 8
+    // of the unit (q = p % 32). Lane tid loads pieces tid + i * WAVES * 64.
+    const int pieces = KS * M * 32;
+    uint32_t src0[XP];
+    int dst0[XP], lim[XP], k0[XP];
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int p = tid + i * WAVES * 64;
+      const int q = p & 31, r = p >> 5;
+      const int m = r % M, slice = r / M;
+      const int su0 = min(slice * sub, nu);
+      lim[i] = p < pieces ? min(sub, nu - su0) : 0;  // units of the piece's slice
+      k0[i] = (u0 + su0) * kUnitK + q * 8;
+      src0[i] = (static_cast<uint32_t>(m) * K + k0[i]) * 2;
+      dst0[i] = p < pieces ? (slice * kRingSlots * M + m) * kRingRow + q * 8 : -1;
+    }
+    // Pieces past the slice's units or past K load as zeros (out of the
+    // buffer's range), so the zero-padded tail of the last unit meets 0.
+    auto load_x = [&](u4 (&r)[XP], int c) {
+#pragma unroll
+      for (int i = 0; i < XP; ++i) {
+        const bool live = c < lim[i] && k0[i] + c * kUnitK < K;
+        r[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, live ? src0[i] + c * (kUnitK * 2) : 0x80000000u, 0, 0);
+      }
+    };
+    auto store_x = [&](const u4 (&r)[XP], int c) {
+#pragma unroll
+      for (int i = 0; i < XP; ++i)
+        if (dst0[i] >= 0) *reinterpret_cast<u4*>(xs + dst0[i] + (c % kRingSlots) * slot_halves) = r[i];
+    };
+    // LDS stores done, then a bare barrier: the loads stay in flight.
+    auto publish = [&]() {
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    // Unit c's pieces live in xr[c % DEPTH] from their load to their store.
+    u4 xr[DEPTH][XP];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) load_x(xr[i], i);
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+      load_unit(buf[i], stream, i, lane);
+      asm volatile("" ::: "memory");
+    }
+    store_x(xr[0], 0);
+    load_x(xr[0], DEPTH);
+    publish();
+    const _Float16* xrow = xs + ks * kRingSlots * slot_halves + min(mcol, M - 1) * kRingRow + g * 64;
+    // Every wavefront runs the same steps (sub, rounded up to DEPTH), so
+    // the barriers match; a wavefront past its own units only stages.
+    for (int base = 0; base < sub; base += DEPTH) {
 #pragma unroll
       for (int i = 0; i < DEPTH; ++i) {
-        if (base + i < wnu) unit_mfma(buf[i], xrow + (base + i) * kUnitK, acc2);
-        load_unit(buf[i], stream, base + DEPTH + i, lane);
-        // keep the scheduler from sinking the refill below the next units' math
+        const int j = base + i;
+        store_x(xr[(i + 1) % DEPTH], j + 1);
+        load_x(xr[(i + 1) % DEPTH], j + 1 + DEPTH);
+        publish();
+        if (active && j < wnu) unit_mfma(buf[i], xrow + (j % kRingSlots) * slot_halves, acc2);
+        load_unit(buf[i], stream, j + DEPTH, lane);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
-
   f4 acc = acc2[0] + acc2[1];
 
   // The KS slices of each n-tile are added through LDS, in slice order, into
@@ -487,8 +582,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   if (argmax) argmax_finish();
 }
 
-template <int FMT, int WAVES, int DEPTH, int EPI>
-hipError_t launch_cfg_e(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
+template <int FMT, int WAVES, int DEPTH, int EPI, int XP>
+hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
                       float tensor_scale, void* y, float* val, void* workspace, int m, int64_t n, int64_t k,
                       hipStream_t stream) {
   const int NT = static_cast<int>(ceil_div(n, kTileN));
@@ -496,7 +591,7 @@ hipError_t launch_cfg_e(const GemmPlan& p, const void* x, const void* packed, co
   const unsigned groups = static_cast<unsigned>(ceil_div(NT, WAVES / p.k_slices));
   // Dynamic LDS above the 64 KiB default must be allowed per kernel.
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH, EPI>),
+      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH, EPI, XP>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBudget));
   if (attr != hipSuccess) return attr;
   char* wsb = static_cast<char*>(workspace);
@@ -509,12 +604,38 @@ hipError_t launch_cfg_e(const GemmPlan& p, const void* x, const void* packed, co
     amax.idx = static_cast<int*>(y);
     amax.val = val;
   }
-  hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH, EPI>), dim3(groups, static_cast<unsigned>(p.split)),
+  hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH, EPI, XP>), dim3(groups, static_cast<unsigned>(p.split)),
                      dim3(WAVES * 64), p.lds_bytes, stream, static_cast<const _Float16*>(x),
                      static_cast<const uint8_t*>(packed), row_scales, tensor_scale,
                      static_cast<_Float16*>(y), ws, counters, amax, m, static_cast<int>(n),
                      static_cast<int>(k), NT, KU, p.units_per_split, p.lds_stride, p.k_slices);
   return hipGetLastError();
+}
+
+// x pieces each thread stages per unit in the ring stage.
+int ring_pieces(int waves, int k_slices, int m) { return (k_slices * m * 32 + waves * 64 - 1) / (waves * 64); }
+
+template <int FMT, int WAVES, int DEPTH, int EPI>
+hipError_t launch_cfg_e(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
+                        float tensor_scale, void* y, float* val, void* workspace, int m, int64_t n, int64_t k,
+                        hipStream_t stream) {
+  if (p.x_stage == kStageFull)
+    return launch_kernel<FMT, WAVES, DEPTH, EPI, 0>(p, x, packed, row_scales, tensor_scale, y, val, workspace, m,
+                                                    n, k, stream);
+  // The ring stage is built for depths 2..4 (the planner allows no other).
+  if constexpr (DEPTH <= 4) {
+    switch (ring_pieces(WAVES, p.k_slices, m)) {
+      case 1:
+        return launch_kernel<FMT, WAVES, DEPTH, EPI, 1>(p, x, packed, row_scales, tensor_scale, y, val, workspace,
+                                                        m, n, k, stream);
+      case 2:
+        return launch_kernel<FMT, WAVES, DEPTH, EPI, 2>(p, x, packed, row_scales, tensor_scale, y, val, workspace,
+                                                        m, n, k, stream);
+      default:
+        break;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int FMT, int WAVES, int DEPTH>
@@ -578,15 +699,15 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
     if (!w.waves) w.waves = t->waves;
     if (!w.k_slices) w.k_slices = t->k_slices;
     if (!w.depth) w.depth = t->depth;
+    if (!w.x_stage) w.x_stage = t->x_stage;
   }
 
-  // K ranges over workgroups: as few as the LDS stage allows.
+  // K ranges over workgroups: as few as a full activation stage allows.
   int64_t split = w.split > 0 ? w.split : (KU ? ceil_div(KU, max_ups) : 1);
   if (split > KU) split = KU ? KU : 1;
   if (split < 1) split = 1;
   const int64_t ups = KU ? ceil_div(KU, split) : 0;
   if (KU) split = ceil_div(KU, ups);
-  if (ups > max_ups) return false;
 
   // n-tiles per workgroup first (from M), then as many K slices per n-tile
   // as the workgroup has room for and the K range supports.
@@ -622,13 +743,30 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   const int depth = w.depth ? w.depth : 3;
   if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
 
+  // Activation stage: the caller's choice is binding; a tuned or automatic
+  // one falls back to the other stage when it is not possible. The ring
+  // stage wins from kRingMinM rows on (its per-unit barriers cost more than
+  // a small full stage saves).
+  const bool full_ok = ups <= max_ups;
+  const bool ring_ok = depth <= 4 && ring_pieces(waves, ks, m) <= kRingMaxPieces &&
+                       2 * static_cast<int64_t>(m) * k < (int64_t(1) << 31);
+  int stage = w.x_stage ? w.x_stage : (m >= kRingMinM ? kStageRing : kStageFull);
+  if (stage != kStageFull && stage != kStageRing) return false;
+  if (!o.x_stage) {
+    if (stage == kStageRing && !ring_ok) stage = kStageFull;
+    if (stage == kStageFull && !full_ok) stage = kStageRing;
+  }
+  if (stage == kStageFull ? !full_ok : !ring_ok) return false;
+
   p->split = static_cast<int>(split);
   p->waves = waves;
   p->depth = depth;
   p->k_slices = ks;
   p->units_per_split = static_cast<int>(ups);
   p->lds_stride = static_cast<int>(ups * kUnitK + kRowPad);
-  p->lds_bytes = static_cast<size_t>(m) * p->lds_stride * sizeof(_Float16);
+  p->x_stage = stage;
+  p->lds_bytes = stage == kStageFull ? static_cast<size_t>(m) * p->lds_stride * sizeof(_Float16)
+                                     : static_cast<size_t>(ks) * kRingSlots * m * kRingRow * sizeof(_Float16);
   // K slices reduce through the same LDS: one 16x16 fp32 tile per wavefront.
   const size_t red_bytes = ks > 1 ? static_cast<size_t>(waves) * 64 * sizeof(f4) : 0;
   if (p->lds_bytes < red_bytes) p->lds_bytes = red_bytes;

@@ -15,7 +15,11 @@ namespace qpn {
 struct LaunchOverride {
   int split = 0, waves = 0, depth = 0, k_slices = 0;  // 0 = automatic
   int epilogue = 0;  // 0: y[M, N]; 1: SwiGLU (h[M, N/2]); 2: greedy argmax per row
+  int x_stage = 0;   // 0 automatic; kStageFull; kStageRing
 };
+
+constexpr int kStageFull = 1;  // the workgroup's whole K range of x staged before the stream
+constexpr int kStageRing = 2;  // a three-unit ring per K slice, refilled alongside the stream
 
 struct GemmPlan {
   int split;
@@ -23,8 +27,9 @@ struct GemmPlan {
   int k_slices;    // wavefronts of a workgroup that split one n-tile's K range
   int depth;       // units of the weight stream each wavefront keeps in flight
   int epilogue;    // 0 y[M, N]; 1 h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:]; 2 argmax of each row
+  int x_stage;     // kStageFull or kStageRing
   int units_per_split;
-  int lds_stride;  // halves per staged activation row
+  int lds_stride;  // halves per staged activation row (full stage)
   size_t lds_bytes;
   // Workspace: one split-K arrival counter per n-tile (padded to 256 bytes),
   // a control block (the argmax epilogue's arrival counters), fp32 partials

@@ -65,14 +65,21 @@ def _w(fmt=q.QPN_FMT_NVFP4, n=512, k=1024, packed=FAKE, rs=FAKE):
     return q.make_weight(fmt, n, k, packed, 1.0, rs)
 
 
-def _gemm(x, w, y, m, ws=None, wsb=0, split=0, waves=0, depth=0, k_slices=0, reserved=0):
-    launch = q.make_launch(split, waves, depth, k_slices)
+def _gemm(x, w, y, m, ws=None, wsb=0, split=0, waves=0, depth=0, k_slices=0, reserved=0, x_stage=0):
+    launch = q.make_launch(split, waves, depth, k_slices, x_stage=x_stage)
     launch.reserved[0] = reserved
     return q.lib().qpn_gemm_tuned(x, ctypes.byref(w), y, m, ws, wsb, ctypes.byref(launch), None)
 
 
-def _ws(w, m, split=0, waves=0, depth=0, k_slices=0):
-    return q.qpn_workspace_bytes_tuned(w, m, q.make_launch(split, waves, depth, k_slices))
+def _ws(w, m, split=0, waves=0, depth=0, k_slices=0, x_stage=0):
+    return q.qpn_workspace_bytes_tuned(w, m, q.make_launch(split, waves, depth, k_slices, x_stage=x_stage))
+
+
+def _plan(w, m, **kw):
+    try:
+        return q.qpn_gemm_plan(w, m, q.make_launch(**kw))
+    except q.QpnError as e:
+        return e.status
 
 
 def test_gemm_rejects_bad_arguments_before_any_device_call():
@@ -91,6 +98,8 @@ def test_gemm_rejects_bad_arguments_before_any_device_call():
     assert _gemm(FAKE, _w(), FAKE, 1, depth=5) == err
     assert _gemm(FAKE, _w(), FAKE, 1, k_slices=3) == err
     assert _gemm(FAKE, _w(), FAKE, 1, reserved=1) == err
+    assert _gemm(FAKE, _w(), FAKE, 1, x_stage=3) == err
+    assert _gemm(FAKE, _w(), FAKE, 1, x_stage=-1) == err
     assert _gemm(FAKE, _w(), FAKE, 1, waves=4, k_slices=8) == q.QPN_ERR_UNSUPPORTED
     w = _w()
     w.reserved = 1
@@ -114,9 +123,13 @@ def test_gemm_workspace_checks():
     # partials [split][m][n]
     counters = (5120 // 16) * 4
     assert _ws(w, 8, split=5) == (counters + 255) // 256 * 256 + CONTROL + 5 * 8 * 5120 * 4
-    # one K range of 17408 x 8 rows does not fit the activation stage in LDS
-    assert _ws(w, 8, split=1) == 0
-    assert _gemm(FAKE, w, FAKE, 8, FAKE, need, split=1) == q.QPN_ERR_UNSUPPORTED
+    # one K range of 17408 x 8 rows does not fit a full activation stage in
+    # LDS; the ring stage takes it (and then no workspace is needed)
+    full, ring = q.QPN_X_STAGE_FULL, q.QPN_X_STAGE_RING
+    assert _ws(w, 8, split=1, x_stage=full) == 0
+    assert _gemm(FAKE, w, FAKE, 8, FAKE, need, split=1, x_stage=full) == q.QPN_ERR_UNSUPPORTED
+    assert _plan(w, 8, split_k=1).x_stage == ring
+    assert _plan(w, 8, split_k=1, x_stage=full) == q.QPN_ERR_UNSUPPORTED
     assert _ws(_w(n=5120, k=4096), 1, split=1) == 0
     assert _ws(_w(n=5120, k=4096), 1, split=1, k_slices=4) == 0     # K slices need no workspace
     # gate_up at M=1 fills the chip without splitting K
@@ -128,18 +141,55 @@ def test_plan_resolves_tuned_and_rule_based_launches():
     # the 27B gate_up at M=1 comes from the tuned table
     p = q.qpn_gemm_plan(_w(n=34816, k=5120), 1)
     assert (p.split_k, p.waves_per_group, p.k_slices, p.depth) == (1, 4, 4, 3)
-    # down at M=8 must split K: 17408 x 8 rows do not fit one LDS stage
-    p = q.qpn_gemm_plan(_w(n=5120, k=17408), 8)
-    assert p.split_k > 1 and p.k_slices >= 1
+    assert p.x_stage == q.QPN_X_STAGE_FULL
     # any other shape goes through the rule: valid values, explicit fields kept
     p = q.qpn_gemm_plan(_w(n=1000, k=3072), 3, q.make_launch(depth=6))
     assert p.depth == 6 and p.waves_per_group in (4, 8) and p.k_slices in (1, 2, 4, 8)
     assert p.waves_per_group % p.k_slices == 0 and p.split_k >= 1
+    full, ring = q.QPN_X_STAGE_FULL, q.QPN_X_STAGE_RING
     for m in range(1, 17):
         p = q.qpn_gemm_plan(_w(n=777, k=17408), m)
-        assert p.split_k * 65536 >= 0 and p.waves_per_group in (4, 8)
-    with pytest.raises(q.QpnError):
-        q.qpn_gemm_plan(_w(n=5120, k=17408), 8, q.make_launch(split_k=1))
+        assert p.split_k >= 1 and p.waves_per_group in (4, 8) and p.x_stage in (full, ring)
+        # a full stage must fit the K range of m rows in LDS
+        if p.x_stage == full:
+            assert 2 * m * (-(-68 // p.split_k) * 256 + 8) <= 79 * 1024
+        else:
+            assert p.depth <= 4 and p.k_slices * m <= 4 * p.waves_per_group
+    # small M stages the whole K range, from 5 rows on the ring takes over
+    assert _plan(_w(n=1000, k=3072), 1).x_stage == full
+    assert _plan(_w(n=1000, k=3072), 4).x_stage == full
+    assert _plan(_w(n=1000, k=3072), 5).x_stage == ring
+    assert _plan(_w(n=1000, k=3072), 8).x_stage == ring
+    # the tuned table picks stages per shape and row count
+    assert _plan(_w(n=151936, k=5120), 8).x_stage == ring
+    assert _plan(_w(n=34816, k=5120), 4).x_stage == full
+    # an automatic stage falls back to what the other fields allow
+    assert _plan(_w(n=1000, k=3072), 8, depth=6).x_stage == full
+    assert _plan(_w(n=1000, k=3072), 16, waves_per_group=4, k_slices=4).x_stage == full
+
+
+def test_ring_stage_limits():
+    unsup = q.QPN_ERR_UNSUPPORTED
+    ring = q.QPN_X_STAGE_RING
+    w = _w(n=1000, k=3072)
+    # depth 2..4 only
+    for d in (2, 3, 4):
+        assert _plan(w, 8, depth=d, x_stage=ring).depth == d
+    for d in (6, 8):
+        assert _plan(w, 8, depth=d, x_stage=ring) == unsup
+    # at most two x pieces per thread: k_slices * m <= 4 * waves
+    assert _plan(w, 16, waves_per_group=4, k_slices=1, x_stage=ring).x_stage == ring
+    assert _plan(w, 16, waves_per_group=4, k_slices=2, x_stage=ring) == unsup
+    assert _plan(w, 16, waves_per_group=8, k_slices=2, x_stage=ring).x_stage == ring
+    assert _plan(w, 16, waves_per_group=8, k_slices=4, x_stage=ring) == unsup
+    assert _plan(w, 1, waves_per_group=4, k_slices=4, x_stage=ring).x_stage == ring
+    # x offsets are 32-bit: 2 * m * k must stay below 2^31
+    big = _w(n=16, k=(1 << 26))
+    assert _plan(big, 16, x_stage=ring) == unsup
+    # the ring needs no split: any K range at any M
+    p = _plan(_w(n=5120, k=17408), 16, split_k=1, waves_per_group=8, k_slices=2, x_stage=ring)
+    assert (p.split_k, p.x_stage) == (1, ring)
+    assert _ws(_w(n=5120, k=17408), 16, split=1, waves=8, k_slices=2, x_stage=ring) == 0
 
 
 def test_swiglu_epilogue_plans_and_checks():

@@ -50,6 +50,57 @@ def test_gemm_launch_shapes_agree(fmt, split, waves, depth, k_slices):
     _parity(fmt, m, n, k, seed=77, split_k=split, waves=waves, depth=depth, k_slices=k_slices)
 
 
+RING = qt.QPN_X_STAGE_RING
+FULL_STAGE = qt.QPN_X_STAGE_FULL
+# ring launches for m = 5: k_slices * m <= 4 * waves, depth 2..4
+RING_LAUNCHES = [(1, 4, 2, 1), (1, 4, 3, 2), (1, 8, 4, 4), (2, 8, 2, 2), (3, 4, 4, 1), (7, 8, 3, 1),
+                 (0, 8, 0, 0), (0, 0, 0, 0)]
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("split,waves,depth,k_slices", RING_LAUNCHES)
+def test_ring_stage_launch_shapes(fmt, split, waves, depth, k_slices):
+    n, k, m = 96, 1792, 5
+    say("gemm ring", fmt, split, waves, depth, k_slices)
+    _parity(fmt, m, n, k, seed=77, split_k=split, waves=waves, depth=depth, k_slices=k_slices, x_stage=RING)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("n,k", SMALL)
+@pytest.mark.parametrize("m", [1, 3, 8, 16])
+def test_ring_stage_parity_small(fmt, m, n, k):
+    """The ring stage on ragged K tails (48, 272, 1552 ...), one-unit K ranges
+    and every row count class."""
+    say("gemm ring small", fmt, m, n, k)
+    _parity(fmt, m, n, k, seed=2000 + n + k + m, x_stage=RING)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("m,n,k,split,waves,k_slices,depth", [
+    (1, 512, 2304, 1, 4, 4, 3), (3, 100, 272, 1, 8, 2, 2), (8, 300, 1280, 1, 8, 2, 4),
+    (8, 1024, 5120, 3, 8, 2, 2), (16, 64, 2304, 1, 8, 2, 3), (16, 640, 4352, 2, 4, 1, 4),
+    (5, 33, 1552, 2, 8, 4, 2)])
+def test_ring_and_full_stage_give_the_same_bits(fmt, m, n, k, split, waves, k_slices, depth):
+    """Both stages feed the same MFMA sequence in the same order: for one
+    launch shape the outputs agree bit for bit."""
+    say("ring vs full", fmt, m, n, k, split, waves, k_slices, depth)
+    w = workloads.weights(n, k, 31 + m)
+    pw, _ = gpu_quantize(fmt, to_dev(w))
+    x = to_dev(workloads.activations(m, k, 32 + m))
+    kw = dict(split_k=split, waves=waves, k_slices=k_slices, depth=depth)
+    y_full = to_host(qt.gemm(x, pw, x_stage=FULL_STAGE, **kw))
+    y_ring = to_host(qt.gemm(x, pw, x_stage=RING, **kw))
+    assert np.array_equal(y_full.view(np.uint16), y_ring.view(np.uint16))
+
+
+def test_ring_stage_takes_a_k_range_the_full_stage_cannot():
+    """down (17408) at 16 rows in one K range: 557 KB of activations per
+    workgroup do not fit LDS, the 3-unit ring does."""
+    n, k, m = 256, 17408, 16
+    say("ring long k", n, k, m)
+    _parity("nvfp4", m, n, k, seed=41, split_k=1, waves=8, k_slices=2, x_stage=RING)
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
 @pytest.mark.parametrize("k_slices", [2, 4, 8])
 def test_k_slices_ragged(fmt, k_slices):

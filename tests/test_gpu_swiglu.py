@@ -48,7 +48,10 @@ def test_swiglu_parity(fmt, m, n, k):
 
 LAUNCHES = [dict(split_k=2, waves=8, depth=2, k_slices=2), dict(split_k=3, waves=4, depth=3, k_slices=1),
             dict(split_k=1, waves=8, depth=3, k_slices=4), dict(split_k=5, waves=8, depth=4, k_slices=1),
-            dict(split_k=1, waves=4, depth=2, k_slices=2)]
+            dict(split_k=1, waves=4, depth=2, k_slices=2),
+            # the ring activation stage (x_stage 2)
+            dict(split_k=1, waves=8, depth=3, k_slices=2, x_stage=2), dict(split_k=3, waves=4, depth=2, k_slices=1, x_stage=2),
+            dict(split_k=1, waves=8, depth=4, k_slices=4, x_stage=2)]
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
