@@ -209,9 +209,16 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *                    per K slice in a ring refilled one unit ahead of the
  *                    stream (one barrier per unit; LDS of
  *                    1584 * m * k_slices bytes; needs depth 2..4,
- *                    k_slices * m <= 4 * waves_per_group and 2 * m * k < 2^31).
- * The result bits depend on split_k and k_slices (the summation order), not
- * on the other fields.
+ *                    k_slices * m <= 4 * waves_per_group and 2 * m * k < 2^31);
+ *   whole_groups     with split_k > 1, the number of leading groups of
+ *                    n-tiles (waves_per_group / k_slices tiles each) that
+ *                    still take all of K in one workgroup; only the others
+ *                    are split (0 = all split; more than there are = none).
+ *                    Whole groups first, then the split ones' ranges: a grid
+ *                    that fills the CUs evenly and leaves a short tail of
+ *                    small workgroups. A full stage must hold all of K.
+ * The result bits depend on split_k, whole_groups and k_slices (the
+ * summation order), not on the other fields.
  */
 typedef enum { QPN_EPILOGUE_NONE = 0, QPN_EPILOGUE_SWIGLU = 1, QPN_EPILOGUE_ARGMAX = 2 } qpn_epilogue;
 typedef enum { QPN_X_STAGE_AUTO = 0, QPN_X_STAGE_FULL = 1, QPN_X_STAGE_RING = 2 } qpn_x_stage;
@@ -223,7 +230,8 @@ typedef struct {
   int32_t k_slices;
   int32_t epilogue;
   int32_t x_stage;
-  int32_t reserved[2]; /* must be 0 */
+  int32_t whole_groups;
+  int32_t reserved; /* must be 0 */
 } qpn_launch;
 
 /* qpn_gemm with an explicit launch shape (NULL = automatic). A shape that

@@ -50,7 +50,8 @@ class qpn_launch(ctypes.Structure):
         ("k_slices", ctypes.c_int32),
         ("epilogue", ctypes.c_int32),
         ("x_stage", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("whole_groups", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -185,8 +186,8 @@ def qpn_workspace_bytes(weight, m):
 
 
 def make_launch(split_k=0, waves_per_group=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE,
-                x_stage=QPN_X_STAGE_AUTO):
-    return qpn_launch(split_k, waves_per_group, depth, k_slices, epilogue, x_stage)
+                x_stage=QPN_X_STAGE_AUTO, whole_groups=0):
+    return qpn_launch(split_k, waves_per_group, depth, k_slices, epilogue, x_stage, whole_groups)
 
 
 def qpn_workspace_bytes_tuned(weight, m, launch):

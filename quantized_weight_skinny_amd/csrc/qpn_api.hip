@@ -155,8 +155,7 @@ namespace {
 
 bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   if (!l) return true;
-  for (int i = 0; i < 2; ++i)
-    if (l->reserved[i] != 0) return false;
+  if (l->reserved != 0 || l->whole_groups < 0) return false;
   if (l->x_stage != QPN_X_STAGE_AUTO && l->x_stage != QPN_X_STAGE_FULL && l->x_stage != QPN_X_STAGE_RING)
     return false;
   if (l->split_k < 0 || l->waves_per_group < 0 || l->depth < 0 || l->k_slices < 0) return false;
@@ -168,6 +167,7 @@ bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   o->k_slices = l->k_slices;
   o->epilogue = l->epilogue;
   o->x_stage = l->x_stage;
+  o->whole_groups = l->whole_groups;
   return true;
 }
 
@@ -200,6 +200,7 @@ qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launc
   resolved->k_slices = p.k_slices;
   resolved->epilogue = p.epilogue;
   resolved->x_stage = p.x_stage;
+  resolved->whole_groups = p.whole_groups;
   return QPN_OK;
 }
 

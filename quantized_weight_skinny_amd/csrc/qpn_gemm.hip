@@ -37,8 +37,8 @@ constexpr size_t kLdsBudget = 79 * 1024;
 // Launch shapes. For the matrices of a ~27B dense decoder (hidden 5120) the
 // launch comes from a table measured on MI355X: a sweep of activation stage x
 // workgroup size x K slices x K split x stream depth, best graph-replayed time
-// per launch at M = 1, 2, 4, 8, 16. Other shapes use a rule distilled from the
-// same sweep:
+// per launch at M = 1, 2, 4, 8, 16 (and, for gate_up, groups kept whole x
+// split of the rest). Other shapes use a rule distilled from the same sweep:
 //  * a workgroup holds TN n-tiles that share one staged copy of x (the
 //    staging reads 2*M bytes of x per K element against 9*TN bytes of NVFP4
 //    weights), TN = 2 up to M = 4 and 4 above;
@@ -48,20 +48,26 @@ constexpr size_t kLdsBudget = 79 * 1024;
 //    cut to fit LDS (that reduction costs memory round trips at the tail);
 //  * a stream depth of 3 units;
 //  * the ring activation stage from kRingMinM rows on (at 8 and 16 rows it
-//    wins on every matrix but one, at 4 it ties with the full stage).
+//    wins on every matrix but one, at 4 it ties with the full stage);
+//  * no whole groups (all groups split alike): a balanced grid needs the
+//    shape's group count, and is only tabled where it was measured.
 struct TunedLaunch {
   int fmt;
   int64_t n, k;
   int m_max;  // entry applies to m <= m_max (entries of a shape in increasing m_max)
   int waves, k_slices, split, depth;
   int x_stage = kStageFull;
+  int whole_groups = 0;
 };
 
 constexpr TunedLaunch kTuned[] = {
-    // NVFP4 gate_up 34816 x 5120
-    {kFmtNvfp4, 34816, 5120, 1, 4, 4, 1, 3}, {kFmtNvfp4, 34816, 5120, 2, 4, 4, 1, 2},
-    {kFmtNvfp4, 34816, 5120, 4, 8, 4, 1, 2}, {kFmtNvfp4, 34816, 5120, 8, 4, 2, 1, 2, kStageRing},
-    {kFmtNvfp4, 34816, 5120, 16, 8, 2, 1, 2, kStageRing},
+    // NVFP4 gate_up 34816 x 5120: 2176 n-tiles. Whole groups of 8 (or 4)
+    // tiles fill the 256 CUs evenly (256 or 512 groups); the last 16 (32)
+    // groups split K four ways, a short tail of small workgroups.
+    {kFmtNvfp4, 34816, 5120, 1, 8, 1, 4, 2, kStageRing, 256},
+    {kFmtNvfp4, 34816, 5120, 2, 4, 1, 4, 2, kStageRing, 512},
+    {kFmtNvfp4, 34816, 5120, 4, 8, 1, 4, 2, kStageRing, 256},
+    {kFmtNvfp4, 34816, 5120, 16, 4, 1, 4, 2, kStageRing, 512},
     // NVFP4 down 5120 x 17408
     {kFmtNvfp4, 5120, 17408, 2, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 17408, 4, 8, 2, 3, 2},
     {kFmtNvfp4, 5120, 17408, 8, 8, 2, 3, 2, kStageRing}, {kFmtNvfp4, 5120, 17408, 16, 8, 2, 3, 2, kStageRing},
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     const _Float16* x, const uint8_t* packed,
     const float* __restrict__ row_scales, float tensor_scale, _Float16* __restrict__ y,
     float* __restrict__ ws, int* __restrict__ counters, ArgmaxOut amax, int M, int N, int K, int NT, int KU,
-    int ups, int stride, int KS) {
+    int ups, int stride, int KS, int groups, int whole, int split) {
   // The epilogue is a template parameter, so the plain kernels carry none of
   // the others: kEpiSwiglu writes h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:],
   // kEpiArgmax writes each row's largest logit and its index.
@@ -216,10 +222,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int S = gridDim.y;
-  const int s = blockIdx.y;
-  const int u0 = s * ups;
-  const int nu = min(KU - u0, ups);
+  // Workgroups [0, whole) each take one group of n-tiles over the whole K;
+  // each of the other groups has its K cut into `split` ranges of `ups`
+  // units, one workgroup per range, range-major (all first ranges, then all
+  // second ranges ...).
+  int grp, s, S;
+  if (static_cast<int>(blockIdx.x) < whole) {
+    grp = blockIdx.x;
+    s = 0;
+    S = 1;
+  } else {
+    const int r = blockIdx.x - whole;
+    const int tail = groups - whole;
+    s = r / tail;
+    grp = whole + (r - s * tail);
+    S = split;
+  }
+  const int u0 = S == 1 ? 0 : s * ups;
+  const int nu = S == 1 ? KU : min(KU - u0, ups);
   // The workgroup's WAVES wavefronts cover TN n-tiles x KS slices of its K
   // range: wavefront (tn, ks) streams n-tile tn over the ks-th slice.
   const int TN = WAVES / KS;
@@ -233,8 +253,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   // others the up tiles holding the same rows + N/2.
   const int half_tn = TN / 2;
   const int NTh = NT / 2;
-  const int pair = blockIdx.x * half_tn + (tn < half_tn ? tn : tn - half_tn);
-  const int nt = swiglu ? (tn < half_tn ? pair : NTh + pair) : blockIdx.x * TN + tn;
+  const int pair = grp * half_tn + (tn < half_tn ? tn : tn - half_tn);
+  const int nt = swiglu ? (tn < half_tn ? pair : NTh + pair) : grp * TN + tn;
   const bool active = swiglu ? pair < NTh : nt < NT;
   const uint32_t unit_stride = static_cast<uint32_t>(NT) * kBytes;
   const Stream stream(packed + unit_offset(active ? nt : 0, u0 + wu0, NT, kBytes),
@@ -446,16 +466,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   auto argmax_finish = [&]() {
     __syncthreads();
     if (tid < M)
-      __hip_atomic_store(amax.keys + static_cast<size_t>(blockIdx.x) * M + tid, best[tid], __ATOMIC_RELAXED,
+      __hip_atomic_store(amax.keys + static_cast<size_t>(grp) * M + tid, best[tid], __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Arrival in two levels, so that thousands of groups do not queue on one
     // counter: group g counts on sub-counter g % kArgmaxSubs (each on its own
     // cache line); the last of each sub-counter's groups counts on the total.
-    const int groups = gridDim.x;
     if (tid == 0) {
-      const int sub = blockIdx.x % kArgmaxSubs;
+      const int sub = grp % kArgmaxSubs;
       const int members = (groups - 1 - sub) / kArgmaxSubs + 1;
       int* sc = amax.done + sub * kCounterStride;
       int last = __hip_atomic_fetch_add(sc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1;
@@ -530,7 +549,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     return;
   }
 
-  // K was split over gridDim.y workgroups per group of n-tiles: publish this
+  // K was split over S workgroups for this group of n-tiles: publish this
   // range's fp32 partials, then the last workgroup of the group to arrive
   // adds all ranges in range order (the same order whichever arrives last, so
   // the result is deterministic) and resets the group's counter for the next
@@ -552,14 +571,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0)
-    last_group = __hip_atomic_fetch_add(counters + blockIdx.x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 S - 1;
+    last_group = __hip_atomic_fetch_add(counters + grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
   __syncthreads();
   if (!last_group) return;
   // Rows of the group: all TN tiles' rows, or (SwiGLU) the gate rows of its
   // TN/2 gate tiles, each combined with its up row N/2 further on.
   const int rows = (swiglu ? half_tn : TN) * kTileN;
-  const int nbase = blockIdx.x * rows;
+  const int nbase = grp * rows;
   const int nend = swiglu ? Nh : N;
   const size_t range_stride = static_cast<size_t>(M) * N;
   for (int idx = tid; idx < M * rows; idx += WAVES * 64) {
@@ -578,7 +596,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
       y[static_cast<size_t>(m) * N + n] = static_cast<_Float16>(sum);
     }
   }
-  if (tid == 0) __hip_atomic_store(counters + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (argmax) argmax_finish();
 }
 
@@ -588,7 +606,9 @@ hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, c
                       hipStream_t stream) {
   const int NT = static_cast<int>(ceil_div(n, kTileN));
   const int KU = static_cast<int>(ceil_div(k, kUnitK));
-  const unsigned groups = static_cast<unsigned>(ceil_div(NT, WAVES / p.k_slices));
+  const int groups = static_cast<int>(ceil_div(NT, WAVES / p.k_slices));
+  const int whole = p.split > 1 ? p.whole_groups : groups;  // groups that take all of K
+  const unsigned grid = static_cast<unsigned>(whole + (groups - whole) * (p.split > 1 ? p.split : 0));
   // Dynamic LDS above the 64 KiB default must be allowed per kernel.
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH, EPI, XP>),
@@ -604,11 +624,11 @@ hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, c
     amax.idx = static_cast<int*>(y);
     amax.val = val;
   }
-  hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH, EPI, XP>), dim3(groups, static_cast<unsigned>(p.split)),
-                     dim3(WAVES * 64), p.lds_bytes, stream, static_cast<const _Float16*>(x),
-                     static_cast<const uint8_t*>(packed), row_scales, tensor_scale,
-                     static_cast<_Float16*>(y), ws, counters, amax, m, static_cast<int>(n),
-                     static_cast<int>(k), NT, KU, p.units_per_split, p.lds_stride, p.k_slices);
+  hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH, EPI, XP>), dim3(grid), dim3(WAVES * 64), p.lds_bytes, stream,
+                     static_cast<const _Float16*>(x), static_cast<const uint8_t*>(packed), row_scales,
+                     tensor_scale, static_cast<_Float16*>(y), ws, counters, amax, m, static_cast<int>(n),
+                     static_cast<int>(k), NT, KU, p.units_per_split, p.lds_stride, p.k_slices, groups, whole,
+                     p.split);
   return hipGetLastError();
 }
 
@@ -700,6 +720,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
     if (!w.k_slices) w.k_slices = t->k_slices;
     if (!w.depth) w.depth = t->depth;
     if (!w.x_stage) w.x_stage = t->x_stage;
+    if (!w.whole_groups && !o.split) w.whole_groups = t->whole_groups;
   }
 
   // K ranges over workgroups: as few as a full activation stage allows.
@@ -743,11 +764,17 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   const int depth = w.depth ? w.depth : 3;
   if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
 
+  // Groups kept whole (split > 1 only): a whole group's workgroup covers
+  // all KU units, so a full stage must hold them.
+  const int64_t groups = ceil_div(NT, waves / ks);
+  const int64_t whole = split > 1 ? (w.whole_groups < groups ? w.whole_groups : groups) : groups;
+  if (w.whole_groups < 0) return false;
+
   // Activation stage: the caller's choice is binding; a tuned or automatic
   // one falls back to the other stage when it is not possible. The ring
   // stage wins from kRingMinM rows on (its per-unit barriers cost more than
   // a small full stage saves).
-  const bool full_ok = ups <= max_ups;
+  const bool full_ok = (split > 1 && whole > 0 ? KU : ups) <= max_ups;
   const bool ring_ok = depth <= 4 && ring_pieces(waves, ks, m) <= kRingMaxPieces &&
                        2 * static_cast<int64_t>(m) * k < (int64_t(1) << 31);
   int stage = w.x_stage ? w.x_stage : (m >= kRingMinM ? kStageRing : kStageFull);
@@ -759,11 +786,12 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   if (stage == kStageFull ? !full_ok : !ring_ok) return false;
 
   p->split = static_cast<int>(split);
+  p->whole_groups = split > 1 ? static_cast<int>(whole) : 0;
   p->waves = waves;
   p->depth = depth;
   p->k_slices = ks;
   p->units_per_split = static_cast<int>(ups);
-  p->lds_stride = static_cast<int>(ups * kUnitK + kRowPad);
+  p->lds_stride = static_cast<int>((split > 1 && whole > 0 ? KU : ups) * kUnitK + kRowPad);
   p->x_stage = stage;
   p->lds_bytes = stage == kStageFull ? static_cast<size_t>(m) * p->lds_stride * sizeof(_Float16)
                                      : static_cast<size_t>(ks) * kRingSlots * m * kRingRow * sizeof(_Float16);

@@ -8,14 +8,16 @@
 namespace qpn {
 
 // Launch plan of one GEMM call: the K range is cut into `split` pieces of
-// `units_per_split` 256-element units; each workgroup of `waves` wavefronts
-// handles `waves` n-tiles of one piece. split > 1 writes fp32 partial sums to
-// the workspace; the last workgroup of a group to finish adds them in piece
-// order.
+// `units_per_split` 256-element units (except for the first `whole_groups`
+// groups of n-tiles, which take all of K in one workgroup); each workgroup of
+// `waves` wavefronts handles `waves / k_slices` n-tiles of one piece. split > 1
+// writes fp32 partial sums to the workspace; the last workgroup of a group to
+// finish adds them in piece order.
 struct LaunchOverride {
   int split = 0, waves = 0, depth = 0, k_slices = 0;  // 0 = automatic
   int epilogue = 0;  // 0: y[M, N]; 1: SwiGLU (h[M, N/2]); 2: greedy argmax per row
   int x_stage = 0;   // 0 automatic; kStageFull; kStageRing
+  int whole_groups = 0;  // with split > 1: leading n-tile groups kept whole (not split)
 };
 
 constexpr int kStageFull = 1;  // the workgroup's whole K range of x staged before the stream
@@ -28,6 +30,7 @@ struct GemmPlan {
   int depth;       // units of the weight stream each wavefront keeps in flight
   int epilogue;    // 0 y[M, N]; 1 h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:]; 2 argmax of each row
   int x_stage;     // kStageFull or kStageRing
+  int whole_groups;  // split > 1: the first whole_groups groups of n-tiles take all of K
   int units_per_split;
   int lds_stride;  // halves per staged activation row (full stage)
   size_t lds_bytes;

@@ -175,21 +175,23 @@ def requantize_fp8_to_nvfp4(codes8, row_scales):
     return codes, scales, s_t
 
 
-def _launch(split_k=0, waves=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE, x_stage=0):
-    if split_k or waves or depth or k_slices or epilogue or x_stage:
-        return make_launch(split_k, waves, depth, k_slices, epilogue, x_stage)
+def _launch(split_k=0, waves=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE, x_stage=0, whole_groups=0):
+    if split_k or waves or depth or k_slices or epilogue or x_stage or whole_groups:
+        return make_launch(split_k, waves, depth, k_slices, epilogue, x_stage, whole_groups)
     return None
 
 
-def workspace_bytes(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, x_stage=0):
-    launch = _launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_SWIGLU if swiglu else QPN_EPILOGUE_NONE, x_stage)
+def workspace_bytes(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, x_stage=0, whole_groups=0):
+    launch = _launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_SWIGLU if swiglu else QPN_EPILOGUE_NONE, x_stage,
+                     whole_groups)
     d = pw.desc()
     return qpn_workspace_bytes_tuned(d, m, launch) if launch is not None else qpn_workspace_bytes(d, m)
 
 
-def new_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, device="cuda", x_stage=0):
+def new_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, device="cuda", x_stage=0,
+                  whole_groups=0):
     """A zeroed workspace for gemm(pw) with m rows (None when none is needed)."""
-    need = workspace_bytes(pw, m, split_k, waves, depth, k_slices, swiglu, x_stage)
+    need = workspace_bytes(pw, m, split_k, waves, depth, k_slices, swiglu, x_stage, whole_groups)
     return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
 
 
@@ -211,35 +213,37 @@ def _run(x, pw, out, workspace, launch, cols):
     return out
 
 
-def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0):
+def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0, whole_groups=0):
     """y[m, n] = x[m, k] @ dequant(W)^T in fp16 through qpn_gemm.
 
     A workspace, when one is needed and not given, is allocated zeroed per
     call; pass one from new_workspace() to reuse it across calls."""
-    return _run(x, pw, out, workspace, _launch(split_k, waves, depth, k_slices, x_stage=x_stage), pw.n)
+    return _run(x, pw, out, workspace,
+                _launch(split_k, waves, depth, k_slices, x_stage=x_stage, whole_groups=whole_groups), pw.n)
 
 
-def gemm_swiglu(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0):
+def gemm_swiglu(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0,
+                whole_groups=0):
     """h[m, n/2] = silu(g) * u with [g | u] = x @ dequant(W)^T (W's first n/2
     rows are the gate projection): the SwiGLU epilogue of qpn_gemm_tuned
     (zero shape fields: the shape qpn_gemm_swiglu uses)."""
-    launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_SWIGLU, x_stage)
+    launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_SWIGLU, x_stage, whole_groups)
     return _run(x, pw, out, workspace, launch, pw.n // 2)
 
 
-def argmax_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, device="cuda", x_stage=0):
+def argmax_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, device="cuda", x_stage=0, whole_groups=0):
     """A zeroed workspace for gemm_argmax(pw) with up to m rows."""
-    launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_ARGMAX, x_stage)
+    launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_ARGMAX, x_stage, whole_groups)
     return torch.zeros(qpn_workspace_bytes_tuned(pw.desc(), m, launch), dtype=torch.uint8, device=device)
 
 
 def gemm_argmax(x, pw, idx=None, val=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0,
-                x_stage=0):
+                x_stage=0, whole_groups=0):
     """(idx int32 [m], val fp32 [m]): each row's largest logit of
     x @ dequant(W)^T and its index, through qpn_gemm_argmax."""
     _cuda(x, torch.float16, "x")
     m = x.shape[0]
-    launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_ARGMAX, x_stage)
+    launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_ARGMAX, x_stage, whole_groups)
     d = pw.desc()
     need = qpn_workspace_bytes_tuned(d, m, launch)
     if workspace is None or workspace.numel() * workspace.element_size() < need:

@@ -67,7 +67,7 @@ def _w(fmt=q.QPN_FMT_NVFP4, n=512, k=1024, packed=FAKE, rs=FAKE):
 
 def _gemm(x, w, y, m, ws=None, wsb=0, split=0, waves=0, depth=0, k_slices=0, reserved=0, x_stage=0):
     launch = q.make_launch(split, waves, depth, k_slices, x_stage=x_stage)
-    launch.reserved[0] = reserved
+    launch.reserved = reserved
     return q.lib().qpn_gemm_tuned(x, ctypes.byref(w), y, m, ws, wsb, ctypes.byref(launch), None)
 
 
@@ -132,16 +132,20 @@ def test_gemm_workspace_checks():
     assert _plan(w, 8, split_k=1, x_stage=full) == q.QPN_ERR_UNSUPPORTED
     assert _ws(_w(n=5120, k=4096), 1, split=1) == 0
     assert _ws(_w(n=5120, k=4096), 1, split=1, k_slices=4) == 0     # K slices need no workspace
-    # gate_up at M=1 fills the chip without splitting K
-    assert q.qpn_workspace_bytes(_w(n=34816, k=5120), 1) == 0
+    # the 27B qkv at M=1 fills the chip without splitting K
+    assert q.qpn_workspace_bytes(_w(n=7168, k=5120), 1) == 0
     assert q.qpn_workspace_bytes(_w(), 17) == 0
 
 
 def test_plan_resolves_tuned_and_rule_based_launches():
-    # the 27B gate_up at M=1 comes from the tuned table
+    # the 27B gate_up at M=1 comes from the tuned table: 256 whole groups of 8
+    # n-tiles, the last 16 groups split K four ways
     p = q.qpn_gemm_plan(_w(n=34816, k=5120), 1)
-    assert (p.split_k, p.waves_per_group, p.k_slices, p.depth) == (1, 4, 4, 3)
-    assert p.x_stage == q.QPN_X_STAGE_FULL
+    assert (p.split_k, p.waves_per_group, p.k_slices, p.depth, p.whole_groups) == (4, 8, 1, 2, 256)
+    assert p.x_stage == q.QPN_X_STAGE_RING
+    # down at M=1: one K range, full stage
+    p = q.qpn_gemm_plan(_w(n=5120, k=17408), 1)
+    assert (p.split_k, p.x_stage, p.whole_groups) == (1, q.QPN_X_STAGE_FULL, 0)
     # any other shape goes through the rule: valid values, explicit fields kept
     p = q.qpn_gemm_plan(_w(n=1000, k=3072), 3, q.make_launch(depth=6))
     assert p.depth == 6 and p.waves_per_group in (4, 8) and p.k_slices in (1, 2, 4, 8)
@@ -162,10 +166,31 @@ def test_plan_resolves_tuned_and_rule_based_launches():
     assert _plan(_w(n=1000, k=3072), 8).x_stage == ring
     # the tuned table picks stages per shape and row count
     assert _plan(_w(n=151936, k=5120), 8).x_stage == ring
-    assert _plan(_w(n=34816, k=5120), 4).x_stage == full
+    assert _plan(_w(n=5120, k=17408), 4).x_stage == full
     # an automatic stage falls back to what the other fields allow
     assert _plan(_w(n=1000, k=3072), 8, depth=6).x_stage == full
     assert _plan(_w(n=1000, k=3072), 16, waves_per_group=4, k_slices=4).x_stage == full
+
+
+def test_whole_groups_plans():
+    unsup, err = q.QPN_ERR_UNSUPPORTED, q.QPN_ERR_INVALID_ARG
+    ring, full = q.QPN_X_STAGE_RING, q.QPN_X_STAGE_FULL
+    w = _w(n=34816, k=5120)                      # 1088 groups of two tiles at waves 4, k_slices 2
+    p = _plan(w, 8, split_k=4, waves_per_group=4, k_slices=2, whole_groups=1024, x_stage=ring)
+    assert (p.split_k, p.whole_groups) == (4, 1024)
+    # more than there are: every group whole (the split stays, with nothing to split)
+    assert _plan(w, 8, split_k=4, waves_per_group=4, k_slices=2, whole_groups=5000, x_stage=ring).whole_groups == 1088
+    # without a split every group is whole anyway
+    assert _plan(w, 8, split_k=1, waves_per_group=4, k_slices=2, whole_groups=7, x_stage=ring).whole_groups == 0
+    # the partials workspace does not depend on it
+    assert _ws(w, 8, split=4, waves=4, k_slices=2, x_stage=ring) == \
+        q.qpn_workspace_bytes_tuned(w, 8, q.make_launch(4, 4, 0, 2, x_stage=ring, whole_groups=1024))
+    # a whole group stages all of K: a full stage of 8 x 5120 does not fit LDS
+    assert _plan(w, 8, split_k=4, waves_per_group=4, k_slices=2, whole_groups=16, x_stage=full) == unsup
+    assert _plan(w, 8, split_k=4, waves_per_group=4, k_slices=2, x_stage=full).x_stage == full
+    assert _plan(w, 1, split_k=4, waves_per_group=4, k_slices=2, whole_groups=16, x_stage=full).whole_groups == 16
+    launch = q.make_launch(4, 4, 0, 2, whole_groups=-1)
+    assert q.lib().qpn_gemm_tuned(FAKE, ctypes.byref(w), FAKE, 8, FAKE, 1 << 30, ctypes.byref(launch), None) == err
 
 
 def test_ring_stage_limits():

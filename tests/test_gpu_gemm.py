@@ -93,6 +93,33 @@ def test_ring_and_full_stage_give_the_same_bits(fmt, m, n, k, split, waves, k_sl
     assert np.array_equal(y_full.view(np.uint16), y_ring.view(np.uint16))
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("m,n,k,split,whole,waves,k_slices,depth,stage", [
+    (8, 1000, 2304, 4, 20, 4, 2, 2, 2),      # 32 groups: 20 whole, 12 split four ways (ragged N)
+    (1, 1000, 2304, 3, 50, 4, 4, 3, 1),      # full stage holding all of K for the whole groups
+    (5, 512, 1552, 2, 7, 8, 2, 3, 2),        # ragged K tail, 8 groups: 7 whole, 1 split
+    (16, 640, 4352, 6, 9, 8, 2, 2, 2),       # 10 groups, one split six ways
+    (3, 96, 1792, 5, 1, 4, 1, 4, 1)])        # 2 groups: one whole, one split five ways
+def test_whole_groups_with_split_k(fmt, m, n, k, split, whole, waves, k_slices, depth, stage):
+    """The leading groups take all of K, the rest split it: every output within
+    the bound, and reuse of the workspace leaves the same bits."""
+    say("whole groups", fmt, m, n, k, split, whole, waves, k_slices, depth, stage)
+    kw = dict(split_k=split, whole_groups=whole, waves=waves, k_slices=k_slices, depth=depth, x_stage=stage)
+    y = _parity(fmt, m, n, k, seed=500 + whole, **kw)
+    # the whole groups' outputs are the unsplit GEMM's bits
+    w = workloads.weights(n, k, 500 + whole)
+    x = to_dev(workloads.activations(m, k, 501 + whole))
+    pw, _ = gpu_quantize(fmt, to_dev(w))
+    y1 = to_host(qt.gemm(x, pw, split_k=1, waves=waves, k_slices=k_slices, depth=depth, x_stage=stage))
+    rows = whole * 16 * (waves // k_slices)
+    assert np.array_equal(y[:, :rows].view(np.uint16), y1[:, :rows].view(np.uint16))
+    ws = qt.new_workspace(pw, m, **kw)
+    again = [to_host(qt.gemm(x, pw, workspace=ws, **kw)) for _ in range(2)]
+    assert np.array_equal(again[0].view(np.uint16), y.view(np.uint16))
+    assert np.array_equal(again[1].view(np.uint16), y.view(np.uint16))
+    assert not to_host(ws[:(-(-n // 16)) * 4]).any()
+
+
 def test_ring_stage_takes_a_k_range_the_full_stage_cannot():
     """down (17408) at 16 rows in one K range: 557 KB of activations per
     workgroup do not fit LDS, the 3-unit ring does."""

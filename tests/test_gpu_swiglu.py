@@ -51,7 +51,10 @@ LAUNCHES = [dict(split_k=2, waves=8, depth=2, k_slices=2), dict(split_k=3, waves
             dict(split_k=1, waves=4, depth=2, k_slices=2),
             # the ring activation stage (x_stage 2)
             dict(split_k=1, waves=8, depth=3, k_slices=2, x_stage=2), dict(split_k=3, waves=4, depth=2, k_slices=1, x_stage=2),
-            dict(split_k=1, waves=8, depth=4, k_slices=4, x_stage=2)]
+            dict(split_k=1, waves=8, depth=4, k_slices=4, x_stage=2),
+            # leading groups whole, the others split
+            dict(split_k=3, waves=4, depth=2, k_slices=1, x_stage=2, whole_groups=5),
+            dict(split_k=2, waves=8, depth=3, k_slices=2, x_stage=1, whole_groups=3)]
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
