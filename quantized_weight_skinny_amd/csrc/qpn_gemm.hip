@@ -79,6 +79,12 @@ constexpr TunedLaunch kTuned[] = {
     // NVFP4 lm_head 151936 x 5120
     {kFmtNvfp4, 151936, 5120, 1, 8, 4, 1, 3}, {kFmtNvfp4, 151936, 5120, 2, 4, 2, 1, 2, kStageRing},
     {kFmtNvfp4, 151936, 5120, 4, 8, 2, 1, 2}, {kFmtNvfp4, 151936, 5120, 16, 8, 1, 1, 2, kStageRing},
+    // Per-GPU shapes of 4-way tensor parallelism (NVFP4): qkv 1792 x 5120,
+    // o_proj 5120 x 1280, gate_up 8704 x 5120, down 5120 x 4352
+    {kFmtNvfp4, 1792, 5120, 1, 4, 4, 1, 3}, {kFmtNvfp4, 1792, 5120, 8, 8, 2, 6, 2},
+    {kFmtNvfp4, 5120, 1280, 8, 8, 4, 1, 2},
+    {kFmtNvfp4, 8704, 5120, 1, 8, 2, 1, 3}, {kFmtNvfp4, 8704, 5120, 8, 4, 2, 6, 2, kStageRing, 256},
+    {kFmtNvfp4, 5120, 4352, 1, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 4352, 8, 8, 4, 1, 2},
     // FP8 qkv 7168 x 5120
     {kFmtFp8, 7168, 5120, 2, 4, 2, 1, 2}, {kFmtFp8, 7168, 5120, 4, 4, 2, 1, 3, kStageRing},
     {kFmtFp8, 7168, 5120, 8, 4, 2, 1, 2, kStageRing}, {kFmtFp8, 7168, 5120, 16, 8, 2, 2, 2, kStageRing},
