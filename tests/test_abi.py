@@ -172,6 +172,45 @@ def test_plan_resolves_tuned_and_rule_based_launches():
     assert _plan(_w(n=1000, k=3072), 16, waves_per_group=4, k_slices=4).x_stage == full
 
 
+TABLED = [(q.QPN_FMT_NVFP4, (34816, 5120)), (q.QPN_FMT_NVFP4, (5120, 17408)), (q.QPN_FMT_NVFP4, (7168, 5120)),
+          (q.QPN_FMT_NVFP4, (5120, 5120)), (q.QPN_FMT_NVFP4, (151936, 5120)), (q.QPN_FMT_NVFP4, (1792, 5120)),
+          (q.QPN_FMT_NVFP4, (5120, 1280)), (q.QPN_FMT_NVFP4, (8704, 5120)), (q.QPN_FMT_NVFP4, (5120, 4352)),
+          (q.QPN_FMT_FP8_E4M3, (7168, 5120)), (q.QPN_FMT_FP8_E4M3, (5120, 5120)),
+          (q.QPN_FMT_FP8_E4M3, (5120, 17408))]
+
+
+@pytest.mark.parametrize("fmt,shape", TABLED)
+def test_every_tabled_shape_resolves_to_a_valid_plan(fmt, shape):
+    """For the shapes the launch table covers, every M = 1..16 (plain, SwiGLU
+    where N allows, argmax) resolves to a launch within the kernel's limits:
+    a full stage fits the 79 KiB LDS budget, a ring stays within its limits,
+    and the workspace covers the split."""
+    n, k = shape
+    w = q.make_weight(fmt, n, k, FAKE, 1.0, FAKE)
+    ku, nt = -(-k // 256), -(-n // 16)
+    epis = [q.QPN_EPILOGUE_NONE, q.QPN_EPILOGUE_ARGMAX] + ([q.QPN_EPILOGUE_SWIGLU] if n % 32 == 0 else [])
+    for m in range(1, 17):
+        for epi in epis:
+            p = q.qpn_gemm_plan(w, m, q.make_launch(epilogue=epi))
+            assert p.waves_per_group in (4, 8) and p.k_slices in (1, 2, 4, 8)
+            assert p.waves_per_group % p.k_slices == 0 and p.depth in (2, 3, 4, 6, 8)
+            ups = -(-ku // p.split_k)
+            assert -(-ku // ups) == p.split_k
+            groups = -(-nt // (p.waves_per_group // p.k_slices))
+            assert 0 <= p.whole_groups <= groups and (p.split_k > 1 or p.whole_groups == 0)
+            if p.x_stage == q.QPN_X_STAGE_FULL:
+                span = ku if (p.split_k > 1 and p.whole_groups > 0) else ups
+                assert 2 * m * (span * 256 + 8) <= 79 * 1024
+            else:
+                assert p.x_stage == q.QPN_X_STAGE_RING
+                assert p.depth <= 4 and p.k_slices * m <= 4 * p.waves_per_group
+            if epi == q.QPN_EPILOGUE_SWIGLU:
+                assert (p.waves_per_group // p.k_slices) % 2 == 0
+            need = q.qpn_workspace_bytes_tuned(w, m, p)
+            if p.split_k > 1:
+                assert need >= p.split_k * m * n * 4
+
+
 def test_whole_groups_plans():
     unsup, err = q.QPN_ERR_UNSUPPORTED, q.QPN_ERR_INVALID_ARG
     ring, full = q.QPN_X_STAGE_RING, q.QPN_X_STAGE_FULL
