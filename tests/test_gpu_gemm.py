@@ -267,12 +267,19 @@ def test_empty_and_degenerate_shapes():
     y = torch.full((2, 4), 7.0, dtype=torch.float16, device=DEV)
     qt.gemm(x, pw, out=y)
     assert not to_host(y).any()
+    # ... through the ring stage too (automatic from 5 rows, or forced)
+    for m, kw in ((8, {}), (2, dict(x_stage=qt.QPN_X_STAGE_RING))):
+        x = torch.zeros((m, 0), dtype=torch.float16, device=DEV)
+        y = torch.full((m, 4), 7.0, dtype=torch.float16, device=DEV)
+        qt.gemm(x, pw, out=y, **kw)
+        assert not to_host(y).any()
     # M = 0 and N = 0 do nothing
     pw2, _ = gpu_quantize("nvfp4", to_dev(workloads.weights(16, 32, 1)))
     qt.gemm(torch.zeros((0, 32), dtype=torch.float16, device=DEV), pw2)
     # N = 1, K = 16: a single block
     _parity("nvfp4", 1, 1, 16, seed=3)
     _parity("fp8", 3, 1, 16, seed=4)
+    _parity("nvfp4", 16, 1, 16, seed=5)          # ring stage, one 16-element block
 
 
 FULL = [
@@ -284,6 +291,7 @@ FULL = [
     ("nvfp4", "lm_head", 1), ("nvfp4", "lm_head", 8),
     ("nvfp4", "gate_up", 16), ("nvfp4", "down", 16), ("fp8", "o_proj", 2), ("nvfp4", "gemv", 1),
     ("nvfp4", "qkv_tp4", 1), ("nvfp4", "o_proj_tp4", 8), ("nvfp4", "gate_up_tp4", 8), ("nvfp4", "down_tp4", 1),
+    ("nvfp4", "gate_up_tp4", 1), ("nvfp4", "down_tp4", 8), ("nvfp4", "qkv_tp4", 8),
 ]
 
 
