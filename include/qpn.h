@@ -213,7 +213,8 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *   whole_groups     with split_k > 1, the number of leading groups of
  *                    n-tiles (waves_per_group / k_slices tiles each) that
  *                    still take all of K in one workgroup; only the others
- *                    are split (0 = all split; more than there are = none).
+ *                    are split (more than there are = none split). 0: the
+ *                    tuned value when split_k is automatic, else all split.
  *                    Whole groups first, then the split ones' ranges: a grid
  *                    that fills the CUs evenly and leaves a short tail of
  *                    small workgroups. A full stage must hold all of K.
