@@ -199,7 +199,8 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *                    one workgroup that split one n-tile's K range and add
  *                    their results through LDS;
  *   epilogue         QPN_EPILOGUE_NONE (y as in qpn_gemm), QPN_EPILOGUE_SWIGLU
- *                    (see qpn_gemm_swiglu) or QPN_EPILOGUE_ARGMAX (only with
+ *                    (see qpn_gemm_swiglu), QPN_EPILOGUE_F32 (y_dev fp32, see
+ *                    qpn_gemm_f32) or QPN_EPILOGUE_ARGMAX (only with
  *                    qpn_gemm_argmax and the workspace / plan queries);
  *   x_stage          how the activation rows reach LDS (0 = automatic):
  *                    QPN_X_STAGE_FULL copies the workgroup's whole K range
@@ -221,7 +222,12 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  * The result bits depend on split_k, whole_groups and k_slices (the
  * summation order), not on the other fields.
  */
-typedef enum { QPN_EPILOGUE_NONE = 0, QPN_EPILOGUE_SWIGLU = 1, QPN_EPILOGUE_ARGMAX = 2 } qpn_epilogue;
+typedef enum {
+  QPN_EPILOGUE_NONE = 0,
+  QPN_EPILOGUE_SWIGLU = 1,
+  QPN_EPILOGUE_ARGMAX = 2,
+  QPN_EPILOGUE_F32 = 3
+} qpn_epilogue;
 typedef enum { QPN_X_STAGE_AUTO = 0, QPN_X_STAGE_FULL = 1, QPN_X_STAGE_RING = 2 } qpn_x_stage;
 
 typedef struct {
@@ -265,6 +271,26 @@ qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launc
  */
 qpn_status qpn_gemm_swiglu(const void* x_dev, const qpn_weight* w, void* h_dev, int32_t m,
                            void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * qpn_gemm with an fp32 output: the scaled fp32 accumulators, not rounded.
+ * This is what a row-parallel tensor-parallel rank hands to its all-reduce
+ * ([P3] "This is a server, not a GEMM screenshot": the pages run 4-way
+ * tensor parallelism): with K split over ranks each rank's y is a partial
+ * sum, and rounding it to fp16 before the sum would round every rank's
+ * part (and could overflow fp16 where the total does not).
+ *   y_dev     fp32 [m][w->n] row-major output (fully overwritten), 4-byte
+ *             aligned.
+ * Other arguments, the workspace and the launch shape as in qpn_gemm, with
+ * the same accumulators: y is the scaled accumulator rounded once to fp32,
+ * where qpn_gemm rounds it once to fp16. Rounding this y to fp16 so gives
+ * qpn_gemm's bits except where y lies exactly halfway between two fp16
+ * values.
+ * qpn_gemm_tuned with launch->epilogue = QPN_EPILOGUE_F32 is the same call
+ * with an explicit shape.
+ */
+qpn_status qpn_gemm_f32(const void* x_dev, const qpn_weight* w, float* y_dev, int32_t m,
+                        void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
  * A greedy output head: the GEMM with, per activation row, the index and the

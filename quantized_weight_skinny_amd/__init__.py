@@ -31,6 +31,7 @@ QPN_MAX_M = 16
 QPN_EPILOGUE_NONE = 0
 QPN_EPILOGUE_SWIGLU = 1
 QPN_EPILOGUE_ARGMAX = 2
+QPN_EPILOGUE_F32 = 3
 QPN_X_STAGE_AUTO = 0
 QPN_X_STAGE_FULL = 1
 QPN_X_STAGE_RING = 2
@@ -95,6 +96,7 @@ SIGNATURES = {
     "qpn_gemm": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
     "qpn_gemm_tuned": (_I32, [_P, _W, _P, _I32, _P, _SZ, _L, _P]),
     "qpn_gemm_swiglu": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
+    "qpn_gemm_f32": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
     "qpn_gemm_argmax": (_I32, [_P, _W, _P, _P, _I32, _P, _SZ, _L, _P]),
     "qpn_read_ceiling": (_I32, [_P, _SZ, _P, _I32, _P]),
     "qpn_read_ceiling_grid": (_I32, []),
@@ -216,6 +218,11 @@ def qpn_gemm_tuned(x, weight, y, m, workspace, workspace_bytes, launch, stream):
 def qpn_gemm_swiglu(x, weight, h, m, workspace, workspace_bytes, stream):
     return _check(lib().qpn_gemm_swiglu(x, ctypes.byref(weight), h, m, workspace, workspace_bytes, stream),
                   "qpn_gemm_swiglu")
+
+
+def qpn_gemm_f32(x, weight, y, m, workspace, workspace_bytes, stream):
+    return _check(lib().qpn_gemm_f32(x, ctypes.byref(weight), y, m, workspace, workspace_bytes, stream),
+                  "qpn_gemm_f32")
 
 
 def qpn_gemm_argmax(x, weight, idx, val, m, workspace, workspace_bytes, launch, stream):

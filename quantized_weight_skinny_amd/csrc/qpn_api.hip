@@ -159,7 +159,8 @@ bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   if (l->x_stage != QPN_X_STAGE_AUTO && l->x_stage != QPN_X_STAGE_FULL && l->x_stage != QPN_X_STAGE_RING)
     return false;
   if (l->split_k < 0 || l->waves_per_group < 0 || l->depth < 0 || l->k_slices < 0) return false;
-  if (l->epilogue != QPN_EPILOGUE_NONE && l->epilogue != QPN_EPILOGUE_SWIGLU && l->epilogue != QPN_EPILOGUE_ARGMAX)
+  if (l->epilogue != QPN_EPILOGUE_NONE && l->epilogue != QPN_EPILOGUE_SWIGLU && l->epilogue != QPN_EPILOGUE_ARGMAX &&
+      l->epilogue != QPN_EPILOGUE_F32)
     return false;
   o->split = l->split_k;
   o->waves = l->waves_per_group;
@@ -208,8 +209,9 @@ qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launc
 
 namespace {
 
-// One GEMM call with launch override o: y_dev is the fp16 output (or, for
-// the argmax epilogue, the int32 indices, with the fp32 values in val_dev).
+// One GEMM call with launch override o: y_dev is the fp16 output (fp32 for
+// the F32 epilogue; for the argmax epilogue the int32 indices, with the fp32
+// values in val_dev).
 qpn_status gemm_call(const void* x_dev, const qpn_weight* w, void* y_dev, float* val_dev, int32_t m,
                      void* workspace_dev, size_t workspace_bytes, const qpn::LaunchOverride& o, void* stream) {
   const qpn_status st = check_weight(w);
@@ -222,7 +224,7 @@ qpn_status gemm_call(const void* x_dev, const qpn_weight* w, void* y_dev, float*
     return QPN_ERR_INVALID_ARG;
   if (o.epilogue == QPN_EPILOGUE_SWIGLU && w->n % 32) return QPN_ERR_INVALID_ARG;
   if (m == 0 || w->n == 0) return QPN_OK;
-  const size_t out_align = o.epilogue == QPN_EPILOGUE_ARGMAX ? 4 : 2;
+  const size_t out_align = o.epilogue == QPN_EPILOGUE_ARGMAX || o.epilogue == QPN_EPILOGUE_F32 ? 4 : 2;
   if (!y_dev || !aligned(y_dev, out_align)) return QPN_ERR_INVALID_ARG;
   if (val_dev && !aligned(val_dev, 4)) return QPN_ERR_INVALID_ARG;
   if (w->k > 0) {
@@ -274,6 +276,13 @@ qpn_status qpn_gemm_swiglu(const void* x_dev, const qpn_weight* w, void* h_dev, 
   qpn_launch l{};
   l.epilogue = QPN_EPILOGUE_SWIGLU;
   return qpn_gemm_tuned(x_dev, w, h_dev, m, workspace_dev, workspace_bytes, &l, stream);
+}
+
+qpn_status qpn_gemm_f32(const void* x_dev, const qpn_weight* w, float* y_dev, int32_t m,
+                        void* workspace_dev, size_t workspace_bytes, void* stream) {
+  qpn_launch l{};
+  l.epilogue = QPN_EPILOGUE_F32;
+  return qpn_gemm_tuned(x_dev, w, y_dev, m, workspace_dev, workspace_bytes, &l, stream);
 }
 
 int32_t qpn_read_ceiling_grid(void) { return qpn::read_ceiling_default_grid(); }

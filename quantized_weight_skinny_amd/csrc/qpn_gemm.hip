@@ -104,7 +104,7 @@ const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
 
 constexpr int kMinSliceUnits = 4;
 constexpr int kRingMinM = 5;
-constexpr int kEpiNone = 0, kEpiSwiglu = 1, kEpiArgmax = 2;  // GemmPlan::epilogue
+constexpr int kEpiNone = 0, kEpiSwiglu = 1, kEpiArgmax = 2, kEpiF32 = 3;  // GemmPlan::epilogue
 // The argmax epilogue's arrival counters in the workspace's control block.
 constexpr int kArgmaxSubs = 64;
 constexpr int kCounterStride = 16;  // ints: one 64-byte line per counter
@@ -209,16 +209,27 @@ struct ArgmaxOut {
   float* val;                // [M] fp32 max logit, or null
 };
 
+// One output element: rounded once to fp16, or with kEpiF32 the scaled fp32
+// accumulator as it is.
+template <int EPI>
+__device__ __forceinline__ void put_out(void* y, size_t i, float v) {
+  if constexpr (EPI == kEpiF32)
+    static_cast<float*>(y)[i] = v;
+  else
+    static_cast<_Float16*>(y)[i] = static_cast<_Float16>(v);
+}
+
 // XP = 0: full stage; XP > 0: ring stage with XP x pieces per thread.
 template <int FMT, int WAVES, int DEPTH, int EPI, int XP>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     const _Float16* x, const uint8_t* packed,
-    const float* __restrict__ row_scales, float tensor_scale, _Float16* __restrict__ y,
+    const float* __restrict__ row_scales, float tensor_scale, void* __restrict__ y,
     float* __restrict__ ws, int* __restrict__ counters, ArgmaxOut amax, int M, int N, int K, int NT, int KU,
     int ups, int stride, int KS, int groups, int whole, int split) {
   // The epilogue is a template parameter, so the plain kernels carry none of
   // the others: kEpiSwiglu writes h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:],
-  // kEpiArgmax writes each row's largest logit and its index.
+  // kEpiArgmax writes each row's largest logit and its index, kEpiF32 writes
+  // y in fp32.
   constexpr bool swiglu = EPI == kEpiSwiglu;
   constexpr bool argmax = EPI == kEpiArgmax;
   extern __shared__ __align__(16) _Float16 xs[];
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     __syncthreads();
     if (owner && tn < half_tn && mcol < M) {
       const f4 u = xch[tn * 64 + lane];
-      _Float16* dst = y + static_cast<size_t>(mcol) * Nh;
+      _Float16* dst = static_cast<_Float16*>(y) + static_cast<size_t>(mcol) * Nh;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int n = n0 + r;
@@ -542,13 +553,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   }
   if (S == 1) {
     if (owner && mcol < M) {
-      _Float16* dst = y + static_cast<size_t>(mcol) * N;
+      const size_t row = static_cast<size_t>(mcol) * N;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int n = n0 + r;
         if (n < N) {
           const float scale = FMT == kFmtNvfp4 ? tensor_scale : row_scales[n];
-          dst[n] = static_cast<_Float16>(acc[r] * scale);
+          put_out<EPI>(y, row + n, acc[r] * scale);
         }
       }
     }
@@ -595,11 +606,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     if (swiglu) {
       const float u = range_sum(src + Nh, range_stride, S) *
                       (FMT == kFmtNvfp4 ? tensor_scale : row_scales[n + Nh]);
-      y[static_cast<size_t>(m) * Nh + n] = static_cast<_Float16>(silu(sum) * u);
+      put_out<EPI>(y, static_cast<size_t>(m) * Nh + n, silu(sum) * u);
     } else if (argmax) {
       __hip_atomic_fetch_max(&best[m], argmax_key(sum, n), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     } else {
-      y[static_cast<size_t>(m) * N + n] = static_cast<_Float16>(sum);
+      put_out<EPI>(y, static_cast<size_t>(m) * N + n, sum);
     }
   }
   if (tid == 0) __hip_atomic_store(counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -632,7 +643,7 @@ hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, c
   }
   hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH, EPI, XP>), dim3(grid), dim3(WAVES * 64), p.lds_bytes, stream,
                      static_cast<const _Float16*>(x), static_cast<const uint8_t*>(packed), row_scales,
-                     tensor_scale, static_cast<_Float16*>(y), ws, counters, amax, m, static_cast<int>(n),
+                     tensor_scale, y, ws, counters, amax, m, static_cast<int>(n),
                      static_cast<int>(k), NT, KU, p.units_per_split, p.lds_stride, p.k_slices, groups, whole,
                      p.split);
   return hipGetLastError();
@@ -675,6 +686,9 @@ hipError_t launch_cfg(const GemmPlan& p, const void* x, const void* packed, cons
     case kEpiArgmax:
       return launch_cfg_e<FMT, WAVES, DEPTH, kEpiArgmax>(p, x, packed, row_scales, tensor_scale, y, val,
                                                           workspace, m, n, k, stream);
+    case kEpiF32:
+      return launch_cfg_e<FMT, WAVES, DEPTH, kEpiF32>(p, x, packed, row_scales, tensor_scale, y, val,
+                                                       workspace, m, n, k, stream);
     default:
       return launch_cfg_e<FMT, WAVES, DEPTH, kEpiNone>(p, x, packed, row_scales, tensor_scale, y, val,
                                                         workspace, m, n, k, stream);
@@ -807,7 +821,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   // ... and (SwiGLU) the up tiles handed to the gate wavefronts.
   const size_t xch_bytes = o.epilogue == kEpiSwiglu ? static_cast<size_t>(waves / ks / 2) * 64 * sizeof(f4) : 0;
   if (p->lds_bytes < xch_bytes) p->lds_bytes = xch_bytes;
-  if (o.epilogue < kEpiNone || o.epilogue > kEpiArgmax) return false;
+  if (o.epilogue < kEpiNone || o.epilogue > kEpiF32) return false;
   p->epilogue = o.epilogue;
   const size_t counters = (static_cast<size_t>(NT) * sizeof(int) + 255) & ~size_t(255);
   p->control_offset = counters;

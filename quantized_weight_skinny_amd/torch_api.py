@@ -9,6 +9,7 @@ import torch
 
 from . import (
     QPN_EPILOGUE_ARGMAX,
+    QPN_EPILOGUE_F32,
     QPN_EPILOGUE_NONE,
     QPN_EPILOGUE_SWIGLU,
     QPN_X_STAGE_AUTO,
@@ -24,6 +25,7 @@ from . import (
     qpn_requantize_fp8_nvfp4,
     qpn_gemm,
     qpn_gemm_argmax,
+    qpn_gemm_f32,
     qpn_gemm_tuned,
     qpn_nvfp4_tensor_scale,
     qpn_pack_fp8,
@@ -49,6 +51,17 @@ def _cuda(t, dtype, name):
     if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
     return t
+
+
+def _output(out, shape, dtype, like, name="out"):
+    """A new output tensor, or the caller's after checking that the kernel's
+    writes fit it."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    _cuda(out, dtype, name)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(out.shape)}")
+    return out
 
 
 class PackedWeight:
@@ -195,11 +208,10 @@ def new_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, 
     return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
 
 
-def _run(x, pw, out, workspace, launch, cols):
+def _run(x, pw, out, workspace, launch, cols, dtype=torch.float16):
     _cuda(x, torch.float16, "x")
     m = x.shape[0]
-    if out is None:
-        out = torch.empty((m, cols), dtype=torch.float16, device=x.device)
+    out = _output(out, (m, cols), dtype, x)
     d = pw.desc()
     need = qpn_workspace_bytes_tuned(d, m, launch) if launch is not None else qpn_workspace_bytes(d, m)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
@@ -220,6 +232,25 @@ def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=
     call; pass one from new_workspace() to reuse it across calls."""
     return _run(x, pw, out, workspace,
                 _launch(split_k, waves, depth, k_slices, x_stage=x_stage, whole_groups=whole_groups), pw.n)
+
+
+def gemm_f32(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0, whole_groups=0):
+    """y[m, n] = x[m, k] @ dequant(W)^T as fp32, not rounded (a row-parallel
+    rank's partial sum): qpn_gemm_f32, or with any shape field set
+    qpn_gemm_tuned with the F32 epilogue."""
+    if not (split_k or waves or depth or k_slices or x_stage or whole_groups):
+        _cuda(x, torch.float16, "x")
+        m = x.shape[0]
+        out = _output(out, (m, pw.n), torch.float32, x)
+        d = pw.desc()
+        need = qpn_workspace_bytes_tuned(d, m, make_launch(epilogue=QPN_EPILOGUE_F32))
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+        qpn_gemm_f32(x.data_ptr(), d, out.data_ptr(), m, workspace.data_ptr() if need else None,
+                     workspace.numel() * workspace.element_size() if need else 0, _stream())
+        return out
+    launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_F32, x_stage, whole_groups)
+    return _run(x, pw, out, workspace, launch, pw.n, torch.float32)
 
 
 def gemm_swiglu(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0,
@@ -248,10 +279,8 @@ def gemm_argmax(x, pw, idx=None, val=None, workspace=None, split_k=0, waves=0, d
     need = qpn_workspace_bytes_tuned(d, m, launch)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
-    if idx is None:
-        idx = torch.empty(m, dtype=torch.int32, device=x.device)
-    if val is None:
-        val = torch.empty(m, dtype=torch.float32, device=x.device)
+    idx = _output(idx, (m,), torch.int32, x, "idx")
+    val = _output(val, (m,), torch.float32, x, "val")
     qpn_gemm_argmax(x.data_ptr(), d, idx.data_ptr(), val.data_ptr(), m, workspace.data_ptr(),
                     workspace.numel() * workspace.element_size(), launch, _stream())
     return idx, val

@@ -282,6 +282,36 @@ def test_swiglu_epilogue_plans_and_checks():
         q.QPN_ERR_INVALID_ARG
 
 
+def test_f32_epilogue_plans_and_checks():
+    # the fp32 output changes no launch choice: shape and workspace are the
+    # plain GEMM's, for tuned and rule-based shapes alike
+    f32 = q.make_launch(epilogue=q.QPN_EPILOGUE_F32)
+    for (n, k) in ((5120, 17408), (5120, 4352), (34816, 5120), (300, 5120), (37, 48)):
+        w = _w(n=n, k=k)
+        for m in (1, 2, 5, 8, 16):
+            a, b = q.qpn_gemm_plan(w, m), q.qpn_gemm_plan(w, m, f32)
+            assert b.epilogue == q.QPN_EPILOGUE_F32
+            b.epilogue = a.epilogue
+            assert bytes(a) == bytes(b), (n, k, m)
+            assert q.qpn_workspace_bytes_tuned(w, m, f32) == q.qpn_workspace_bytes(w, m)
+    # fp32 output: 4-byte alignment, checked before any device work
+    w = _w(n=48, k=256)
+    assert q.lib().qpn_gemm_f32(FAKE, ctypes.byref(w), FAKE + 2, 1, None, 0, None) == q.QPN_ERR_INVALID_ARG
+    assert q.lib().qpn_gemm_tuned(FAKE, ctypes.byref(w), FAKE + 2, 1, None, 0, ctypes.byref(f32), None) == \
+        q.QPN_ERR_INVALID_ARG
+    assert q.lib().qpn_gemm_f32(FAKE, ctypes.byref(w), FAKE, q.QPN_MAX_M + 1, None, 0, None) == \
+        q.QPN_ERR_INVALID_ARG
+    # a split launch still needs its workspace
+    sp = q.make_launch(split_k=2, epilogue=q.QPN_EPILOGUE_F32)
+    assert q.lib().qpn_gemm_tuned(FAKE, ctypes.byref(_w(n=512, k=1024)), FAKE, 1, None, 0, ctypes.byref(sp),
+                                  None) == q.QPN_ERR_INVALID_ARG
+    # epilogue values past the last are argument errors
+    bad = q.make_launch(epilogue=q.QPN_EPILOGUE_F32 + 1)
+    assert q.lib().qpn_gemm_tuned(FAKE, ctypes.byref(w), FAKE, 1, None, 0, ctypes.byref(bad), None) == \
+        q.QPN_ERR_INVALID_ARG
+    assert q.qpn_workspace_bytes_tuned(w, 1, bad) == 0
+
+
 def test_argmax_epilogue_checks_and_workspace():
     am = q.make_launch(epilogue=q.QPN_EPILOGUE_ARGMAX)
     w = _w(n=151936, k=5120)
