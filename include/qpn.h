@@ -88,10 +88,12 @@ size_t qpn_packed_bytes(int32_t format, int64_t n, int64_t k);
  *   packed_dev       output, packed_bytes >= qpn_packed_bytes(NVFP4, n, k),
  *                    16-byte aligned. Every byte of the packed form is written.
  *   bad_codes_dev    NULL, or a device int32 to which the kernel adds the
- *                    number of NaN block-scale codes (0x7F / 0xFF) it found;
- *                    the caller zeroes it first and checks it after the stream
- *                    is synchronized. NaN scales make their block's outputs
- *                    NaN; they never make the GEMM fault.
+ *                    number of invalid block-scale codes it found: NaN (0x7F,
+ *                    0xFF) or sign-set (0x80..0xFF; NVFP4 block scales are
+ *                    positive). The caller zeroes it first and checks it after
+ *                    the stream is synchronized. Such scales are packed as
+ *                    they are and only give wrong (NaN or negated) outputs
+ *                    for their block; they never make the GEMM fault.
  * The pages keep published FP4 regions in their own format rather than
  * converting them ([P3] "v1.0 got us here. v1.1 removes its last
  * compromise."); this entry point takes such codes as they are.
@@ -101,7 +103,8 @@ qpn_status qpn_pack_nvfp4(const uint8_t* codes_dev, const uint8_t* block_scales_
                           int32_t* bad_codes_dev, void* stream);
 
 /* Canonical FP8 -> packed layout. codes_dev: uint8 [n][k] row-major E4M3FN
- * codes. bad_codes_dev as for qpn_pack_nvfp4 (counts 0x7F / 0xFF codes).
+ * codes. bad_codes_dev as for qpn_pack_nvfp4, counting the NaN codes 0x7F
+ * and 0xFF (weights of either sign are valid).
  * The per-row fp32 scales stay in a separate caller-owned array. ([P3] "v1.0
  * got us here. v1.1 removes its last compromise.": FP8 regions keep FP8.) */
 qpn_status qpn_pack_fp8(const uint8_t* codes_dev, int64_t n, int64_t k,

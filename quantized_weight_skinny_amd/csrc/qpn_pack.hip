@@ -37,6 +37,17 @@ __device__ __forceinline__ int count_nan_e4m3(uint32_t w, int nbytes) {
   return bad;
 }
 
+// NVFP4 block scales are positive E4M3 values: a NaN code or any code with
+// the sign bit set (including -0) is invalid.
+__device__ __forceinline__ int count_bad_block_scales(uint32_t w, int nbytes) {
+  int bad = 0;
+  for (int i = 0; i < nbytes; ++i) {
+    const uint32_t b = (w >> (8 * i)) & 0xFFu;
+    bad += b >= 0x80u || b == 0x7Fu;
+  }
+  return bad;
+}
+
 // One thread per 32-code chunk (16 bytes) of a padded row.
 __global__ __launch_bounds__(kBlock) void pack_nvfp4_codes(const uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ packed, int64_t N,
@@ -80,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void pack_nvfp4_scales(const uint8_t* __res
   }
   *reinterpret_cast<uint32_t*>(packed + unit_offset(nt, u, NT, kNvUnitBytes) + 2048 + (g * 16 + r) * 4) = w;
   if (bad) {
-    const int nb = count_nan_e4m3(w, nvalid);
+    const int nb = count_bad_block_scales(w, nvalid);
     if (nb) atomicAdd(bad, nb);
   }
 }

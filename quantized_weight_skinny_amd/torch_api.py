@@ -53,6 +53,20 @@ def _cuda(t, dtype, name):
     return t
 
 
+def _count(t, count, name):
+    """The kernels read exactly `count` elements of t: refuse any other size."""
+    if t.numel() != count:
+        raise ValueError(f"{name} must hold {count} elements, not {t.numel()}")
+
+
+def _activations(x, pw):
+    """x fp16 [m, K] on the device, K the weight's (the kernels read m * K halves)."""
+    _cuda(x, torch.float16, "x")
+    if x.dim() != 2 or x.shape[1] != pw.k:
+        raise ValueError(f"x must have shape (m, {pw.k}), not {tuple(x.shape)}")
+    return x.shape[0]
+
+
 def _output(out, shape, dtype, like, name="out"):
     """A new output tensor, or the caller's after checking that the kernel's
     writes fit it."""
@@ -88,13 +102,15 @@ class PackedWeight:
 def _raise_bad(bad, where):
     count = int(bad.item())
     if count:
-        raise QpnError(QPN_ERR_BAD_CODE, f"{where}: {count} NaN E4M3 code(s)")
+        raise QpnError(QPN_ERR_BAD_CODE, f"{where}: {count} invalid E4M3 code(s) (NaN, or a sign-set block scale)")
 
 
 def pack_nvfp4(codes, block_scales, tensor_scale, n, k, check=True):
     """Canonical NVFP4 codes [n, k/2] + E4M3 block scales [n, k/16] -> PackedWeight."""
     _cuda(codes, torch.uint8, "codes")
     _cuda(block_scales, torch.uint8, "block_scales")
+    _count(codes, n * (k // 2), "codes")
+    _count(block_scales, n * (k // 16), "block_scales")
     nbytes = qpn_packed_bytes(QPN_FMT_NVFP4, n, k)
     packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
     bad = torch.zeros(1, dtype=torch.int32, device=codes.device) if check else None
@@ -109,6 +125,8 @@ def pack_fp8(codes, row_scales, n, k, check=True):
     """Canonical E4M3 codes [n, k] + fp32 row scales [n] -> PackedWeight."""
     _cuda(codes, torch.uint8, "codes")
     _cuda(row_scales, torch.float32, "row_scales")
+    _count(codes, n * k, "codes")
+    _count(row_scales, n, "row_scales")
     nbytes = qpn_packed_bytes(QPN_FMT_FP8_E4M3, n, k)
     packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
     bad = torch.zeros(1, dtype=torch.int32, device=codes.device) if check else None
@@ -178,6 +196,7 @@ def requantize_fp8_to_nvfp4(codes8, row_scales):
     _cuda(codes8, torch.uint8, "codes")
     _cuda(row_scales, torch.float32, "row_scales")
     n, k = codes8.shape
+    _count(row_scales, n, "row_scales")
     amax = torch.empty(1, dtype=torch.float32, device=codes8.device)
     qpn_fp8_absmax(codes8.data_ptr(), row_scales.data_ptr(), n, k, amax.data_ptr(), _stream())
     s_t = qpn_nvfp4_tensor_scale(float(amax.item()))
@@ -209,8 +228,7 @@ def new_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, 
 
 
 def _run(x, pw, out, workspace, launch, cols, dtype=torch.float16):
-    _cuda(x, torch.float16, "x")
-    m = x.shape[0]
+    m = _activations(x, pw)
     out = _output(out, (m, cols), dtype, x)
     d = pw.desc()
     need = qpn_workspace_bytes_tuned(d, m, launch) if launch is not None else qpn_workspace_bytes(d, m)
@@ -239,8 +257,7 @@ def gemm_f32(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_sli
     rank's partial sum): qpn_gemm_f32, or with any shape field set
     qpn_gemm_tuned with the F32 epilogue."""
     if not (split_k or waves or depth or k_slices or x_stage or whole_groups):
-        _cuda(x, torch.float16, "x")
-        m = x.shape[0]
+        m = _activations(x, pw)
         out = _output(out, (m, pw.n), torch.float32, x)
         d = pw.desc()
         need = qpn_workspace_bytes_tuned(d, m, make_launch(epilogue=QPN_EPILOGUE_F32))
@@ -272,8 +289,7 @@ def gemm_argmax(x, pw, idx=None, val=None, workspace=None, split_k=0, waves=0, d
                 x_stage=0, whole_groups=0):
     """(idx int32 [m], val fp32 [m]): each row's largest logit of
     x @ dequant(W)^T and its index, through qpn_gemm_argmax."""
-    _cuda(x, torch.float16, "x")
-    m = x.shape[0]
+    m = _activations(x, pw)
     launch = make_launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_ARGMAX, x_stage, whole_groups)
     d = pw.desc()
     need = qpn_workspace_bytes_tuned(d, m, launch)

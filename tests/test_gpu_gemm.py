@@ -258,6 +258,39 @@ def test_output_guard_bytes_untouched():
     assert np.all(tail == np.float16(12345.0))
 
 
+def test_binding_refuses_sizes_the_kernels_would_overrun():
+    """The torch binding checks every tensor a kernel reads or writes against
+    the weight's shape before any launch."""
+    say("binding size checks")
+    n, k, m = 48, 512, 2
+    w = workloads.weights(n, k, 16)
+    pw, (codes, scales, _) = gpu_quantize("nvfp4", to_dev(w))
+    x = to_dev(workloads.activations(m, k, 17))
+    for bad_x in (x[:, :k - 16].contiguous(), x.reshape(-1), torch.zeros((m, k + 16), dtype=torch.float16,
+                                                                            device=DEV)):
+        for call in (qt.gemm, qt.gemm_f32, qt.gemm_argmax):
+            with pytest.raises(ValueError):
+                call(bad_x, pw)
+    with pytest.raises(ValueError):
+        qt.gemm_swiglu(x[:, :256].contiguous(), pw)
+    with pytest.raises(ValueError):
+        qt.gemm_argmax(x, pw, idx=torch.empty(m - 1, dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError):
+        qt.pack_nvfp4(codes[: n - 1].contiguous(), scales, 1.0, n, k)
+    with pytest.raises(ValueError):
+        qt.pack_nvfp4(codes, scales[:, :-1].contiguous(), 1.0, n, k)
+    c8, rs = qt.quantize_fp8(to_dev(w))
+    with pytest.raises(ValueError):
+        qt.pack_fp8(c8, rs[:-1].contiguous(), n, k)
+    with pytest.raises(ValueError):
+        qt.pack_fp8(c8[:, :-16].contiguous(), rs, n, k)
+    with pytest.raises(ValueError):
+        qt.requantize_fp8_to_nvfp4(c8, rs[:-1].contiguous())
+    # the well-formed calls still run
+    assert qt.gemm(x, pw).shape == (m, n)
+    assert qt.pack_fp8(c8, rs, n, k).n == n
+
+
 def test_empty_and_degenerate_shapes():
     say("degenerate shapes")
     # K = 0: the empty sum

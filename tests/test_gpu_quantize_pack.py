@@ -115,9 +115,10 @@ PACK_SHAPES = [(512, 1024), (17, 48), (33, 272), (16, 256), (1, 16), (130, 4112)
 def test_pack_unpack_nvfp4_round_trip(n, k):
     say("pack nvfp4", n, k)
     codes = workloads.random_nibble_bytes(n, k, n * 7 + k)
-    scales = workloads.random_block_scale_codes(n, k, n * 11 + k, lo=0, hi=0xFE)
-    scales = np.where((scales & 0x7F) == 0x7F, scales ^ 1, scales).astype(np.uint8)
-    pw = qt.pack_nvfp4(to_dev(codes), to_dev(scales), 1.0, n, k)
+    # every byte value, valid or not, must survive the layout (check=False
+    # skips the count of invalid scale codes, which has its own test)
+    scales = workloads.random_block_scale_codes(n, k, n * 11 + k, lo=0, hi=0xFF)
+    pw = qt.pack_nvfp4(to_dev(codes), to_dev(scales), 1.0, n, k, check=False)
     c2, s2 = qt.unpack(pw)
     assert np.array_equal(to_host(c2), codes)
     assert np.array_equal(to_host(s2), scales)
@@ -147,16 +148,27 @@ def test_pack_unpack_fp8_round_trip(n, k):
     assert np.array_equal(to_host(c2), codes)
 
 
-def test_pack_counts_nan_codes():
-    say("pack nan codes")
+def test_pack_counts_invalid_codes():
+    say("pack invalid codes")
     n, k = 32, 512
     codes = workloads.random_nibble_bytes(n, k, 3)
     scales = workloads.random_block_scale_codes(n, k, 4)
-    scales[3, 5] = 0x7F
-    scales[30, 31] = 0xFF
+    scales[3, 5] = 0x7F          # NaN
+    scales[30, 31] = 0xFF        # NaN
     with pytest.raises(QpnError) as e:
         qt.pack_nvfp4(to_dev(codes), to_dev(scales), 1.0, n, k)
-    assert e.value.status == QPN_ERR_BAD_CODE and "2 NaN" in str(e.value)
+    assert e.value.status == QPN_ERR_BAD_CODE and ": 2 invalid" in str(e.value)
+    # block scales are positive: sign-set codes (-0 included) are invalid too
+    scales[0, 0] = 0x80
+    scales[7, 2] = 0xB8
+    scales[31, 0] = 0xFE
+    with pytest.raises(QpnError) as e:
+        qt.pack_nvfp4(to_dev(codes), to_dev(scales), 1.0, n, k)
+    assert ": 5 invalid" in str(e.value)
+    # the largest and smallest valid scales pass
+    ok = workloads.random_block_scale_codes(n, k, 5)
+    ok[0, 0], ok[1, 1], ok[2, 2] = 0x00, 0x7E, 0x01
+    qt.pack_nvfp4(to_dev(codes), to_dev(ok), 1.0, n, k)
     f8 = workloads.random_fp8_codes(n, k, 5)
     f8[0, 0] = 0x7F
     with pytest.raises(QpnError):
