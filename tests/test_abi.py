@@ -282,6 +282,23 @@ def test_swiglu_epilogue_plans_and_checks():
         q.QPN_ERR_INVALID_ARG
 
 
+def test_packed_size_limit():
+    """The kernel's unit offsets are 32-bit: a weight whose packed form
+    reaches 2 GiB is refused before any device work, one n-tile less is
+    planned (the GPU test runs those largest weights)."""
+    unsup = q.QPN_ERR_UNSUPPORTED
+    for fmt, n_ok in ((q.QPN_FMT_NVFP4, 233008), (q.QPN_FMT_FP8_E4M3, 131056)):
+        k = 16384
+        assert q.qpn_packed_bytes(fmt, n_ok, k) < 2 ** 31 <= q.qpn_packed_bytes(fmt, n_ok + 16, k)
+        for m in (1, 8, 16):
+            assert isinstance(_plan(_w(fmt, n_ok, k), m), q.qpn_launch)
+            assert _plan(_w(fmt, n_ok + 16, k), m) == unsup
+            assert q.qpn_workspace_bytes(_w(fmt, n_ok + 16, k), m) == 0
+        big = _w(fmt, n_ok + 16, k)
+        assert q.lib().qpn_gemm(FAKE, ctypes.byref(big), FAKE, 1, FAKE, 1 << 30, None) == unsup
+        assert q.lib().qpn_gemm_f32(FAKE, ctypes.byref(big), FAKE, 1, FAKE, 1 << 30, None) == unsup
+
+
 def test_f32_epilogue_plans_and_checks():
     # the fp32 output changes no launch choice: shape and workspace are the
     # plain GEMM's, for tuned and rule-based shapes alike

@@ -11,6 +11,7 @@ import oracle
 import workloads
 from gpu_helpers import (DEV, assert_within_tolerance, gpu_quantize, oracle_quantize, oracle_y,
                          say, to_dev, to_host)
+import quantized_weight_skinny_amd as q
 from quantized_weight_skinny_amd import torch_api as qt
 
 pytestmark = pytest.mark.gpu
@@ -233,6 +234,34 @@ def test_negation_and_repeat_are_bit_exact():
         assert np.array_equal(yn, -y1)
 
 
+def test_scale_doubling_and_row_permutation_are_exact():
+    """Closed forms of y = x W~^T on the device: doubling the NVFP4 tensor
+    scale (or the FP8 row scales) doubles the fp32 output exactly, and
+    permuting W's rows permutes y's columns bit for bit (an output's
+    arithmetic does not depend on where its row sits)."""
+    say("scale doubling / row permutation")
+    n, k, m = 304, 2304, 5
+    w = to_dev(workloads.weights(n, k, 31))
+    x = to_dev(workloads.activations(m, k, 32))
+    codes, scales, s_t = qt.quantize_nvfp4(w)
+    c8, rs = qt.quantize_fp8(w)
+    packs = {
+        "nvfp4": lambda idx, f: qt.pack_nvfp4(codes[idx].contiguous(), scales[idx].contiguous(), f * s_t, n, k),
+        "fp8": lambda idx, f: qt.pack_fp8(c8[idx].contiguous(), (f * rs[idx]).contiguous(), n, k),
+    }
+    ident = torch.arange(n, device=DEV)
+    perm = np.random.default_rng(33).permutation(n)
+    pt = torch.from_numpy(perm).to(DEV)
+    for fmt, pack in packs.items():
+        pw, pw2, pwp = pack(ident, 1.0), pack(ident, 2.0), pack(pt, 1.0)
+        for kw in ({}, dict(split_k=3), dict(k_slices=4, waves=8)):
+            y1 = to_host(qt.gemm_f32(x, pw, **kw))
+            assert np.array_equal(to_host(qt.gemm_f32(x, pw2, **kw)), 2 * y1), (fmt, kw)
+            y = to_host(qt.gemm(x, pw, **kw))
+            yp = to_host(qt.gemm(x, pwp, **kw))
+            assert np.array_equal(yp.view(np.uint16), y[:, perm].view(np.uint16)), (fmt, kw)
+
+
 def test_rows_of_a_batch_match_single_row_calls():
     say("batch rows")
     n, k = 128, 1024
@@ -326,6 +355,53 @@ FULL = [
     ("nvfp4", "qkv_tp4", 1), ("nvfp4", "o_proj_tp4", 8), ("nvfp4", "gate_up_tp4", 8), ("nvfp4", "down_tp4", 1),
     ("nvfp4", "gate_up_tp4", 1), ("nvfp4", "down_tp4", 8), ("nvfp4", "qkv_tp4", 8),
 ]
+
+
+# The largest weights the kernel addresses: packed size just under 2 GiB
+# (unit offsets are 32-bit); one more n-tile is refused (a CPU test).
+LARGEST = [("nvfp4", 233008, 16384), ("fp8", 131056, 16384)]
+
+
+@pytest.mark.parametrize("fmt,n,k", LARGEST)
+def test_largest_packed_weights(fmt, n, k):
+    """Canonical codes drawn on the host, packed on the GPU; the oracle
+    recomputes sampled output columns, the last n-tile included."""
+    say("largest packed weight", fmt, n, k)
+    if fmt == "nvfp4":
+        codes = workloads.random_nibble_bytes(n, k, 41)
+        scales = workloads.random_block_scale_codes(n, k, 42, lo=0x30, hi=0x40)
+        s_t = 0.0078125
+        pw = qt.pack_nvfp4(to_dev(codes), to_dev(scales), s_t, n, k)
+    else:
+        codes = workloads.random_fp8_codes(n, k, 43)
+        rs = np.full(n, 0.0078125, np.float32)
+        pw = qt.pack_fp8(to_dev(codes), to_dev(rs), n, k)
+    assert pw.packed.numel() < 2 ** 31
+    torch.cuda.empty_cache()
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n),
+                                     np.random.default_rng(n).integers(0, n, 32)]))
+    for m in (1, 8):
+        x = workloads.activations(m, k, 44 + m)
+        y = to_host(qt.gemm(to_dev(x), pw))
+        if fmt == "nvfp4":
+            y_ref, b = oracle.gemm_nvfp4(x, oracle.unpack_nibbles(codes[cols]), scales[cols], s_t)
+        else:
+            y_ref, b = oracle.gemm_fp8(x, codes[cols], rs[cols])
+        assert_within_tolerance(y[:, cols], y_ref, b, f"{fmt} {n}x{k} m={m}")
+        assert np.isfinite(y).all()
+    del pw
+    torch.cuda.empty_cache()
+
+
+def test_long_k_splits_into_many_ranges():
+    """K = 2^20 with 16 rows: the automatic plan cuts K into a couple of
+    hundred ranges, all added by the last workgroup to arrive."""
+    n, k, m = 40, 1 << 20, 16
+    say("long K", n, k, m)
+    plan = q.qpn_gemm_plan(q.make_weight(q.QPN_FMT_NVFP4, n, k, None), m)
+    assert plan.split_k > 100
+    _parity("nvfp4", m, n, k, seed=51)
+    _parity("fp8", 3, n, k, seed=52)
 
 
 @pytest.mark.parametrize("fmt,matrix,m", FULL)
