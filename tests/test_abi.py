@@ -5,6 +5,7 @@ include/qpn.h, and rejects bad arguments on the host before any HIP call
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -30,6 +31,41 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, name), name
         assert name in q.SIGNATURES, name
     assert set(q.SIGNATURES) == set(declared)
+
+
+def test_header_compiles_as_c99_and_links(tmp_path):
+    """A plain C99 program includes qpn.h, links against libqpn.so with every
+    declared entry point taken by address, and sees the struct layouts the
+    Python binding uses (host-only calls, no device work)."""
+    src = os.path.join(ROOT, "tests", "c_consumer", "qpn_c_consumer.c")
+    text = open(src).read()
+    for name in _declared_functions():
+        assert f"(entry_fn){name}," in text, name
+    libdir = os.path.dirname(q.LIB_PATH)
+    exe = str(tmp_path / "qpn_c_consumer")
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"), src,
+           "-o", exe, "-L", libdir, "-lqpn", f"-Wl,-rpath,{libdir}"]
+    if os.path.isdir("/opt/rocm/lib"):
+        cmd.append("-Wl,-rpath-link,/opt/rocm/lib")
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stderr
+    got = dict(line.split(" ", 1) for line in run.stdout.splitlines())
+    assert got["ok"] == "1"
+    assert int(got["entries"]) == len(_declared_functions())
+    assert int(got["sizeof_weight"]) == ctypes.sizeof(q.qpn_weight)
+    assert int(got["offset_weight_n"]) == q.qpn_weight.n.offset
+    assert int(got["offset_weight_packed"]) == q.qpn_weight.packed.offset
+    assert int(got["offset_weight_tensor_scale"]) == q.qpn_weight.tensor_scale.offset
+    assert int(got["offset_weight_row_scales"]) == q.qpn_weight.row_scales.offset
+    assert int(got["sizeof_launch"]) == ctypes.sizeof(q.qpn_launch)
+    assert int(got["offset_launch_whole_groups"]) == q.qpn_launch.whole_groups.offset
+    assert int(got["max_m"]) == q.QPN_MAX_M
+    w = _w(n=34816, k=5120)
+    p = q.qpn_gemm_plan(w, 1)
+    assert [int(v) for v in got["plan_gate_up_m1"].split()] == [
+        p.split_k, p.waves_per_group, p.depth, p.k_slices, p.epilogue, p.x_stage, p.whole_groups]
+    assert int(got["workspace_gate_up_m8"]) == q.qpn_workspace_bytes(w, 8)
 
 
 def test_status_strings():
