@@ -9,8 +9,9 @@
 // codes (or two dwords of 8 E4M3 codes), converted with
 // v_cvt_scalef32_pk_f16_fp{4,8}, multiplied by its fp16 block scale and fed
 // as the A operand of v_mfma_f32_16x16x32_f16. The activation rows ride in
-// the B operand (columns 0..M-1 of the 16-wide tile; the rest are zero), so
-// one instruction serves any M <= 16 and the verify rows of a speculative
+// the B operand (columns 0..M-1 of the 16-wide tile; the others repeat row
+// M-1 and are never stored, since MFMA columns do not mix), so one
+// instruction serves any M <= 16 and the verify rows of a speculative
 // round cost no extra weight traffic (the 8-row tile of the post's Volta
 // design becomes the 16-row MFMA tile here).
 //
@@ -24,7 +25,8 @@
 // flight per wavefront. When K is cut into several ranges the fp32 partial
 // tiles go to a workspace and the last workgroup of each group of n-tiles to
 // finish adds them in range order, which keeps the result deterministic and
-// needs no second kernel.
+// needs no second kernel. The epilogue scales the sums and rounds them once
+// to fp16 (or keeps them fp32), or fuses SwiGLU or a greedy argmax.
 #include "qpn_device.hpp"
 #include "qpn_internal.hpp"
 
