@@ -127,7 +127,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // LDS read wait for all outstanding loads, the weight stream included. The
 // caller waits for these loads explicitly before the workgroup barrier.
 // (Untracked older loads can only make the compiler's own waits stricter,
-// since the counter retires loads in issue order.)
+// since the counter retires loads in issue order.) M0 is a reserved register
+// to the compiler, which ignores it in a clobber list: this is safe only
+// because nothing else in these kernels uses M0 (no LDS-DMA builtins, message
+// sends or indirect register indexing); the generated code holds no M0 write
+// other than this one.
 __device__ __forceinline__ void lds_dma16(const void* src, _Float16* lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(lds_dst))));

@@ -119,11 +119,12 @@ __global__ __launch_bounds__(kBlock) void pack_fp8_codes(const uint8_t* __restri
   }
 }
 
+// One thread per 32-code chunk of a row (total = n * KU * 8, so every row
+// index is below n).
 __global__ __launch_bounds__(kBlock) void unpack_nvfp4_kernel(const uint8_t* __restrict__ packed,
                                                               uint8_t* __restrict__ codes,
-                                                              uint8_t* __restrict__ scales,
-                                                              int64_t N, int64_t K, int64_t NT,
-                                                              int64_t KU, int64_t total) {
+                                                              uint8_t* __restrict__ scales, int64_t K,
+                                                              int64_t NT, int64_t KU, int64_t total) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (idx >= total) return;
   const int64_t n = idx / (KU * 8);
@@ -146,9 +147,10 @@ __global__ __launch_bounds__(kBlock) void unpack_nvfp4_kernel(const uint8_t* __r
   }
 }
 
+// One thread per 16-code chunk of a row (total = n * KU * 16).
 __global__ __launch_bounds__(kBlock) void unpack_fp8_kernel(const uint8_t* __restrict__ packed,
-                                                            uint8_t* __restrict__ codes, int64_t N,
-                                                            int64_t K, int64_t NT, int64_t KU, int64_t total) {
+                                                            uint8_t* __restrict__ codes, int64_t K,
+                                                            int64_t NT, int64_t KU, int64_t total) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (idx >= total) return;
   const int64_t n = idx / (KU * 16);
@@ -355,7 +357,7 @@ hipError_t launch_unpack_nvfp4(const void* packed, int64_t n, int64_t k, uint8_t
   if (n == 0 || KU == 0) return hipSuccess;
   const int64_t t = n * KU * 8;
   hipLaunchKernelGGL(unpack_nvfp4_kernel, dim3(blocks_for(t)), dim3(kBlock), 0, stream,
-                     static_cast<const uint8_t*>(packed), codes, scales, n, k, NT, KU, t);
+                     static_cast<const uint8_t*>(packed), codes, scales, k, NT, KU, t);
   return hipGetLastError();
 }
 
@@ -365,7 +367,7 @@ hipError_t launch_unpack_fp8(const void* packed, int64_t n, int64_t k, uint8_t* 
   if (n == 0 || KU == 0) return hipSuccess;
   const int64_t t = n * KU * 16;
   hipLaunchKernelGGL(unpack_fp8_kernel, dim3(blocks_for(t)), dim3(kBlock), 0, stream,
-                     static_cast<const uint8_t*>(packed), codes, n, k, NT, KU, t);
+                     static_cast<const uint8_t*>(packed), codes, k, NT, KU, t);
   return hipGetLastError();
 }
 
