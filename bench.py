@@ -435,8 +435,9 @@ def cpu_baseline(rows):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU (--gpus > 1) is not "
-                                   "part of this build", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the library has no collective "
+                                   "(the all-reduce of a row-parallel layer), so --gpus > 1 is refused",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

@@ -33,7 +33,7 @@ extern "C" {
 typedef enum {
   QPN_OK = 0,
   QPN_ERR_INVALID_ARG = -1,      /* null / misaligned pointer, bad size or format */
-  QPN_ERR_UNSUPPORTED = -2,      /* valid request this build does not implement  */
+  QPN_ERR_UNSUPPORTED = -2,      /* valid request the library does not implement */
   QPN_ERR_BAD_CODE = -3,         /* reserved: invalid codes are counted, see pack */
   QPN_ERR_BUFFER_TOO_SMALL = -4, /* packed buffer or workspace below the required size */
   QPN_ERR_HIP = -5               /* a HIP runtime call failed */
