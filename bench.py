@@ -48,7 +48,7 @@ class mark:
     _lib = None
 
     def __init__(self, name):
-        self.name = name.encode()
+        self.name = name.encode() if name else None
         if mark._lib is None:
             import ctypes
             mark._lib = False
@@ -60,19 +60,19 @@ class mark:
                     continue
 
     def __enter__(self):
-        if mark._lib:
+        if mark._lib and self.name:
             mark._lib.roctxRangePushA(self.name)
 
     def __exit__(self, *exc):
-        if mark._lib:
+        if mark._lib and self.name:
             mark._lib.roctxRangePop()
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--quick", action="store_true", help="only the headline step (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=1024, help="rows per matrix in the CPU oracle sample")
@@ -161,17 +161,63 @@ def capture(launches):
     return g
 
 
-def time_matrix(mat, m, reps=3, label=None, swiglu=False, argmax=False):
-    """Average µs per launch of one matrix: a graph of back-to-back launches
-    over all rotating copies, timed with events on the launch stream.
+# Sustained streaming first: MI355X's clocks dip for about ten milliseconds
+# after a streaming load starts and then settle (a graph of gate_up launches
+# at M=1 goes 18.3 -> 23 -> 18.1 µs per launch over its first 25 replays, and
+# again after a second of idle), so every measurement below is preceded by at
+# least this much untimed work of the same kind, enqueued back to back with
+# the timed part.
+SETTLE_MS = 30.0
+
+
+def settle(run, min_ms=SETTLE_MS):
+    """Enqueue run() (one unit of the work about to be measured) repeatedly,
+    untimed, until about min_ms of GPU time; returns without synchronizing,
+    so the timed work follows on the stream with no idle gap."""
+    import torch
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    run()
+    e1.record(s)
+    torch.cuda.synchronize()
+    once = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(int(np.ceil(min_ms / once))):
+        run()
+
+
+def replay_us(g, per_replay, trials, stat="median", label=None):
+    """µs per launch over `trials` replays of graph g (per_replay launches
+    each), after replays that settle the clocks, timed with events on the
+    launch stream between replays: the median of the per-replay means, or
+    (stat="mean") the mean over all. `label` names the timed replays as a
+    ROCTx range."""
+    import torch
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
+    settle(g.replay)
+    with mark(label):
+        ev[0].record(s)
+        for i in range(trials):
+            g.replay()
+            ev[i + 1].record(s)
+        torch.cuda.synchronize()
+    if stat == "mean":
+        return ev[0].elapsed_time(ev[-1]) * 1e3 / (trials * per_replay)
+    return float(np.median([ev[i].elapsed_time(ev[i + 1]) * 1e3 / per_replay for i in range(trials)]))
+
+
+def time_matrix(mat, m, reps=10, label=None, swiglu=False, argmax=False, stat="median"):
+    """µs per launch of one matrix: a graph of back-to-back launches over all
+    rotating copies, replayed `reps` times with events on the launch stream
+    (the median over replays, or stat="mean": the average launch).
     ``swiglu``: the gate_up GEMM with the SwiGLU epilogue (output n/2 wide);
     ``argmax``: the greedy-argmax epilogue (an index and a value per row)."""
     tag = "_swiglu" if swiglu else "_argmax" if argmax else ""
-    with mark(label or f"{mat.fmt}_m{m}/{mat.name}{tag}"):
-        return _time_matrix(mat, m, reps, swiglu, argmax)
+    return _time_matrix(mat, m, reps, swiglu, argmax, stat, label or f"{mat.fmt}_m{m}/{mat.name}{tag}")
 
 
-def _time_matrix(mat, m, reps, swiglu=False, argmax=False):
+def _time_matrix(mat, m, reps, swiglu=False, argmax=False, stat="median", label=None):
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
     x = torch.randn((m, mat.k), device="cuda").half()
@@ -190,50 +236,35 @@ def _time_matrix(mat, m, reps, swiglu=False, argmax=False):
     g = capture(launches)
     g.replay()
     torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(reps):
-        g.replay()
-    e1.record(s)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * len(launches))
+    us = replay_us(g, len(launches), reps, stat, label)
     del g
     return us, mat.bytes_for(m, swiglu, argmax) / (us * 1e-6) / 1e9
 
 
-def time_mlp(gate_up, down, m, reps=3):
+def time_mlp(gate_up, down, m, reps=10):
     """The MLP of one layer as the decoder runs it: x -> gate_up with the
     SwiGLU epilogue -> h -> down -> y, over the rotating copies, one graph.
     Returns (µs per MLP, GB/s over weights + x + h written and read + y)."""
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
-    with mark(f"nvfp4_m{m}/mlp_swiglu"):
-        x = torch.randn((m, gate_up.k), device="cuda").half()
-        h = torch.empty((m, gate_up.n // 2), dtype=torch.float16, device="cuda")
-        y = torch.empty((m, down.n), dtype=torch.float16, device="cuda")
-        ws_g = qt.new_workspace(gate_up.copies[0], m, swiglu=True)
-        ws_d = qt.new_workspace(down.copies[0], m)
-        r = min(len(gate_up.copies), len(down.copies))
+    x = torch.randn((m, gate_up.k), device="cuda").half()
+    h = torch.empty((m, gate_up.n // 2), dtype=torch.float16, device="cuda")
+    y = torch.empty((m, down.n), dtype=torch.float16, device="cuda")
+    ws_g = qt.new_workspace(gate_up.copies[0], m, swiglu=True)
+    ws_d = qt.new_workspace(down.copies[0], m)
+    r = min(len(gate_up.copies), len(down.copies))
 
-        def mlp(i):
-            qt.gemm_swiglu(x, gate_up.copies[i], out=h, workspace=ws_g)
-            qt.gemm(h, down.copies[i], out=y, workspace=ws_d)
+    def mlp(i):
+        qt.gemm_swiglu(x, gate_up.copies[i], out=h, workspace=ws_g)
+        qt.gemm(h, down.copies[i], out=y, workspace=ws_d)
 
-        for i in range(r):
-            mlp(i)
-        g = capture([(lambda i=i: mlp(i)) for i in range(r)])
-        g.replay()
-        torch.cuda.synchronize()
-        s = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        for _ in range(reps):
-            g.replay()
-        e1.record(s)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * r)
-        del g
+    for i in range(r):
+        mlp(i)
+    g = capture([(lambda i=i: mlp(i)) for i in range(r)])
+    g.replay()
+    torch.cuda.synchronize()
+    us = replay_us(g, r, reps, label=f"nvfp4_m{m}/mlp_swiglu")
+    del g
     nbytes = gate_up.bytes_for(m, swiglu=True) + down.bytes_for(m)
     return us, nbytes / (us * 1e-6) / 1e9
 
@@ -252,6 +283,7 @@ def read_ceiling(nbytes=4 << 30, reps=6):
         torch.cuda.synchronize()
         s = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        settle(lambda: qt.read_ceiling(buf, grid, sink))
         e0.record(s)
         for _ in range(reps):
             qt.read_ceiling(buf, grid, sink)
@@ -281,6 +313,7 @@ def read_ceiling_sized(nbytes, total=4 << 30, reps=2):
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settle(g.replay)
     e0.record(s)
     for _ in range(reps):
         g.replay()
@@ -366,10 +399,16 @@ def decode_step(ms=(1, 2, 4, 8), reps=3):
         s = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         # stream-ordered: the launches issued one by one from the host
-        with mark(f"decode_m{m}/stream"):
+        for fn in launches:
+            fn()
+        torch.cuda.synchronize()
+
+        def one_step():
             for fn in launches:
                 fn()
-            torch.cuda.synchronize()
+
+        settle(one_step)
+        with mark(f"decode_m{m}/stream"):
             e0.record(s)
             for _ in range(reps):
                 for fn in launches:
@@ -378,10 +417,11 @@ def decode_step(ms=(1, 2, 4, 8), reps=3):
             torch.cuda.synchronize()
         ms_stream = e0.elapsed_time(e1) / reps
         # one HIP graph holding the whole step
+        g = capture(launches)
+        g.replay()
+        torch.cuda.synchronize()
+        settle(g.replay)
         with mark(f"decode_m{m}/graph"):
-            g = capture(launches)
-            g.replay()
-            torch.cuda.synchronize()
             e0.record(s)
             for _ in range(reps):
                 g.replay()
@@ -472,37 +512,49 @@ def main():
         qt.gemm(x1, gate_up.copies[i % r_steps], out=h, workspace=ws_g)
         qt.gemm(x2, down.copies[i % r_steps], out=y, workspace=ws_d)
 
-    # The warmup and the timed steps are each one HIP graph (W and K steps,
-    # cycling through the rotating copies), so no Python launch overhead
-    # sits between the kernels; the graph is checked against the eager step.
+    # One HIP graph holds one cycle of steps (every rotating copy once); the W
+    # warmup steps and the K timed steps are back-to-back replays of it, plus
+    # a graph of the leftover steps when W or K is not a whole number of
+    # cycles. Small graphs replayed back to back keep the GPU streaming with
+    # no idle; one graph of thousands of launches does not. The cycle graph
+    # is checked against the eager step first.
     for i in range(r_steps):
         step(i)
     torch.cuda.synchronize()
     eager_y = y.clone()
-    warm = capture([(lambda i=i: step(i)) for i in range(max(args.warmup, 1))])
-    timed = capture([(lambda i=i: step(i)) for i in range(args.steps)])
-    with mark("step/warmup"):
-        warm.replay()
-        torch.cuda.synchronize()
+    cycle = capture([(lambda i=i: step(i)) for i in range(r_steps)])
+    leftover = {n % r_steps: capture([(lambda i=i: step(i)) for i in range(n % r_steps)])
+                for n in (args.warmup, args.steps) if n % r_steps}
+    cycle.replay()
+    torch.cuda.synchronize()
     if not torch.equal(y, eager_y):
         raise SystemExit("graph replay does not reproduce the eager step")
+
+    def run_steps(n):
+        for _ in range(n // r_steps):
+            cycle.replay()
+        if n % r_steps:
+            leftover[n % r_steps].replay()
+
     s = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with mark("step/warmup"):
+        run_steps(args.warmup)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     with mark("step/timed"):
         t0.record(s)
-        timed.replay()
+        run_steps(args.steps)
         t1.record(s)
         torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    del warm, timed
+    del cycle, leftover
 
     # The dominant kernel (gate_up): a graph of back-to-back launches over
     # the rotating copies, events on the launch stream around it.
-    gate_up_us, achieved = time_matrix(gate_up, m, reps=2, label="roofline/nvfp4_m1/gate_up")
+    gate_up_us, achieved = time_matrix(gate_up, m, reps=10, label="roofline/nvfp4_m1/gate_up", stat="mean")
     traffic = kernel_traffic()
     log(f"step {ms_step * 1e3:.1f} us, {value:.0f} GB/s; gate_up {gate_up_us:.1f} us per launch, "
         f"{achieved:.0f} GB/s; wall {wall:.3f} s; traffic {traffic}")
