@@ -77,8 +77,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=1024, help="rows per matrix in the CPU oracle sample")
     p.add_argument("--launches", default="",
-                   help="profiling mode: comma-separated fmt:matrix:m[:full|ring] cases, each launched --steps "
-                        "times in order (after one warm-up launch), then exit")
+                   help="profiling mode: comma-separated fmt:matrix:m[:full|ring|dot] cases (dot: the VALU "
+                        "packed-dot path, full stage), each launched --steps times in order (after one warm-up "
+                        "launch), then exit")
     return p.parse_args()
 
 
@@ -89,24 +90,25 @@ def run_launches(spec, steps):
     import torch
     import quantized_weight_skinny_amd as q
     from quantized_weight_skinny_amd import torch_api as qt
-    stages = {"": 0, "full": q.QPN_X_STAGE_FULL, "ring": q.QPN_X_STAGE_RING}
+    stages = {"": 0, "full": q.QPN_X_STAGE_FULL, "ring": q.QPN_X_STAGE_RING, "dot": q.QPN_X_STAGE_FULL}
     done = []
     for case in spec.split(","):
         fmt, name, m, *rest = case.split(":")
         m, stage = int(m), stages[rest[0] if rest else ""]
+        dot = int(bool(rest) and rest[0] == "dot")
         n, k = workloads.SHAPES[name]
         nbytes = q.qpn_packed_bytes(q.QPN_FMT_NVFP4 if fmt == "nvfp4" else q.QPN_FMT_FP8_E4M3, n, k)
         mat = Mat(name, fmt, "launches", copies=max(2, int(np.ceil(300e6 / nbytes))))
         x = torch.randn((m, mat.k), device="cuda").half()
         y = torch.empty((m, mat.n), dtype=torch.float16, device="cuda")
-        ws = qt.new_workspace(mat.copies[0], m, x_stage=stage)
-        plan = q.qpn_gemm_plan(mat.copies[0].desc(), m, q.make_launch(x_stage=stage))
+        ws = qt.new_workspace(mat.copies[0], m, x_stage=stage, valu_dot=dot)
+        plan = q.qpn_gemm_plan(mat.copies[0].desc(), m, q.make_launch(x_stage=stage, valu_dot=dot))
         for i in range(steps + 1):
-            qt.gemm(x, mat.copies[i % len(mat.copies)], out=y, workspace=ws, x_stage=stage)
+            qt.gemm(x, mat.copies[i % len(mat.copies)], out=y, workspace=ws, x_stage=stage, valu_dot=dot)
         torch.cuda.synchronize()
         done.append({"case": case, "dispatches": steps + 1, "split_k": plan.split_k, "waves": plan.waves_per_group,
                      "k_slices": plan.k_slices, "depth": plan.depth, "x_stage": plan.x_stage,
-                     "whole_groups": plan.whole_groups})
+                     "whole_groups": plan.whole_groups, "valu_dot": plan.valu_dot})
         log(f"{case}: {steps + 1} launches, plan {done[-1]}")
         del mat
         torch.cuda.empty_cache()

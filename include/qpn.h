@@ -221,9 +221,18 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *                    tuned value when split_k is automatic, else all split.
  *                    Whole groups first, then the split ones' ranges: a grid
  *                    that fills the CUs evenly and leaves a short tail of
- *                    small workgroups. A full stage must hold all of K.
- * The result bits depend on split_k, whole_groups and k_slices (the
- * summation order), not on the other fields.
+ *                    small workgroups. A full stage must hold all of K;
+ *   valu_dot         0: the matrix cores (v_mfma_f32_16x16x32_f16, the
+ *                    default); 1: the VALU packed-dot path instead
+ *                    (v_dot2c_f32_f16: each lane adds its row's weight pairs
+ *                    times the m activation rows, so its cost grows with m).
+ *                    It takes m <= 4, QPN_EPILOGUE_NONE, depth 2..4 and a full
+ *                    stage (automatic stage = full; a ring returns
+ *                    QPN_ERR_UNSUPPORTED). It exists to measure the MFMA
+ *                    choice against; qpn_gemm never picks it. Other values
+ *                    return QPN_ERR_INVALID_ARG.
+ * The result bits depend on split_k, whole_groups, k_slices and valu_dot
+ * (the summation order), not on the other fields.
  */
 typedef enum {
   QPN_EPILOGUE_NONE = 0,
@@ -241,7 +250,7 @@ typedef struct {
   int32_t epilogue;
   int32_t x_stage;
   int32_t whole_groups;
-  int32_t reserved; /* must be 0 */
+  int32_t valu_dot;
 } qpn_launch;
 
 /* qpn_gemm with an explicit launch shape (NULL = automatic). A shape that

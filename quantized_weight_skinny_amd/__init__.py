@@ -52,7 +52,7 @@ class qpn_launch(ctypes.Structure):
         ("epilogue", ctypes.c_int32),
         ("x_stage", ctypes.c_int32),
         ("whole_groups", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("valu_dot", ctypes.c_int32),
     ]
 
 
@@ -188,8 +188,8 @@ def qpn_workspace_bytes(weight, m):
 
 
 def make_launch(split_k=0, waves_per_group=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE,
-                x_stage=QPN_X_STAGE_AUTO, whole_groups=0):
-    return qpn_launch(split_k, waves_per_group, depth, k_slices, epilogue, x_stage, whole_groups)
+                x_stage=QPN_X_STAGE_AUTO, whole_groups=0, valu_dot=0):
+    return qpn_launch(split_k, waves_per_group, depth, k_slices, epilogue, x_stage, whole_groups, valu_dot)
 
 
 def qpn_workspace_bytes_tuned(weight, m, launch):

@@ -155,7 +155,7 @@ namespace {
 
 bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   if (!l) return true;
-  if (l->reserved != 0 || l->whole_groups < 0) return false;
+  if ((l->valu_dot != 0 && l->valu_dot != 1) || l->whole_groups < 0) return false;
   if (l->x_stage != QPN_X_STAGE_AUTO && l->x_stage != QPN_X_STAGE_FULL && l->x_stage != QPN_X_STAGE_RING)
     return false;
   if (l->split_k < 0 || l->waves_per_group < 0 || l->depth < 0 || l->k_slices < 0) return false;
@@ -169,6 +169,7 @@ bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   o->epilogue = l->epilogue;
   o->x_stage = l->x_stage;
   o->whole_groups = l->whole_groups;
+  o->valu_dot = l->valu_dot;
   return true;
 }
 
@@ -202,6 +203,7 @@ qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launc
   resolved->epilogue = p.epilogue;
   resolved->x_stage = p.x_stage;
   resolved->whole_groups = p.whole_groups;
+  resolved->valu_dot = p.dot_rows ? 1 : 0;
   return QPN_OK;
 }
 

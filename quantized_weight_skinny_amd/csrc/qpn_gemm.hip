@@ -207,6 +207,61 @@ __device__ __forceinline__ void unit_mfma(const Unit<kFmtFp8>& w, const _Float16
   }
 }
 
+// The VALU packed-dot alternative to the MFMA (a launch option, measured
+// against it): lane (r = lane % 16, g = lane / 16) holds the 64 weights of
+// row r in K group g, as fp16 pairs straight from the converts, and adds R
+// activation rows' dot products with v_dot2c_f32_f16 (two products and the
+// fp32 accumulator per instruction, R per weight pair). The NVFP4 block
+// scale multiplies each 16-element block's partial sum once, in fp32. xr[m]
+// is row m's staged x at the lane's K group; `off` the unit's offset in it.
+__device__ __forceinline__ float dot8(const h8& a, const h8& b, float c) {
+  c = __builtin_amdgcn_fdot2(h2{a[0], a[1]}, h2{b[0], b[1]}, c, false);
+  c = __builtin_amdgcn_fdot2(h2{a[2], a[3]}, h2{b[2], b[3]}, c, false);
+  c = __builtin_amdgcn_fdot2(h2{a[4], a[5]}, h2{b[4], b[5]}, c, false);
+  return __builtin_amdgcn_fdot2(h2{a[6], a[7]}, h2{b[6], b[7]}, c, false);
+}
+
+template <int R>
+__device__ __forceinline__ void unit_dot(const Unit<kFmtNvfp4>& w, const _Float16* const (&xr)[R], int off,
+                                         float (&acc)[R]) {
+  const h2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.sc, 1.0f, false);
+  const h2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.sc, 1.0f, true);
+  const float bs[4] = {static_cast<float>(s01.x), static_cast<float>(s01.y), static_cast<float>(s23.x),
+                       static_cast<float>(s23.y)};
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    float part[R];
+#pragma unroll
+    for (int m = 0; m < R; ++m) part[m] = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = 2 * blk + tt;
+      const uint32_t d = word(t < 4 ? w.c0 : w.c1, t & 3);
+      const h8 a = cat(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0),
+                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1),
+                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2),
+                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3));
+#pragma unroll
+      for (int m = 0; m < R; ++m) part[m] = dot8(a, x_fragment(xr[m] + off + t * 8), part[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < R; ++m) acc[m] = fmaf(bs[blk], part[m], acc[m]);
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void unit_dot(const Unit<kFmtFp8>& w, const _Float16* const (&xr)[R], int off,
+                                         float (&acc)[R]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const u4& v = w.q[t >> 1];
+    const int i = (t & 1) * 2;
+    const h8 a = decode_fp8x8(word(v, i), word(v, i + 1));
+#pragma unroll
+    for (int m = 0; m < R; ++m) acc[m] = dot8(a, x_fragment(xr[m] + off + t * 8), acc[m]);
+  }
+}
+
 // Outputs of the greedy-argmax epilogue and its workspace.
 struct ArgmaxOut {
   unsigned long long* keys;  // [groups][M]: each group's best key per row
@@ -226,7 +281,9 @@ __device__ __forceinline__ void put_out(void* y, size_t i, float v) {
 }
 
 // XP = 0: full stage; XP > 0: ring stage with XP x pieces per thread.
-template <int FMT, int WAVES, int DEPTH, int EPI, int XP>
+// DOT = 0: MFMA; DOT > 0: the VALU packed-dot path for up to DOT rows (full
+// stage and the plain epilogue only).
+template <int FMT, int WAVES, int DEPTH, int EPI, int XP, int DOT>
 __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     const _Float16* x, const uint8_t* packed,
     const float* __restrict__ row_scales, float tensor_scale, void* __restrict__ y,
@@ -290,6 +347,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   const int mcol = lane & 15;
   const int g = lane >> 4;
   f4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  static_assert(DOT == 0 || (XP == 0 && EPI == kEpiNone), "packed-dot path: full stage, plain epilogue");
+  constexpr int kDotRows = DOT > 0 ? DOT : 1;
+  float dacc[kDotRows];
+#pragma unroll
+  for (int m = 0; m < kDotRows; ++m) dacc[m] = 0.f;
   // Loads of the weight stream are never conditional: a unit past the
   // wavefront's range lies past the stream's byte range, so the buffer load
   // returns zeros without touching memory. This keeps the compiler's view of
@@ -344,6 +406,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     asm volatile("" ::: "memory");
 
     const _Float16* xrow = xs + min(mcol, M - 1) * stride + g * 64 + wu0 * kUnitK;
+    const _Float16* xr[kDotRows];
+#pragma unroll
+    for (int m = 0; m < kDotRows; ++m) xr[m] = xs + min(m, M - 1) * stride + g * 64 + wu0 * kUnitK;
     if (active) {
       // Each slot of buf is consumed and then refilled in place (unit u +
       // DEPTH goes where unit u was), so the loop carries no register copies
@@ -351,7 +416,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
       for (int base = 0; base < wnu; base += DEPTH) {
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i) {
-          if (base + i < wnu) unit_mfma(buf[i], xrow + (base + i) * kUnitK, acc2);
+          if (base + i < wnu) {
+            if constexpr (DOT > 0)
+              unit_dot<kDotRows>(buf[i], xr, (base + i) * kUnitK, dacc);
+            else
+              unit_mfma(buf[i], xrow + (base + i) * kUnitK, acc2);
+          }
           load_unit(buf[i], stream, base + DEPTH + i, lane);
           // keep the scheduler from sinking the refill below the next units' math
           __builtin_amdgcn_sched_barrier(0);
@@ -437,6 +507,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     }
   }
   f4 acc = acc2[0] + acc2[1];
+  if constexpr (DOT > 0) {
+    // Packed-dot path: add the four K groups' sums of each row (lanes 16
+    // apart), then move them to the MFMA's output layout, where lane
+    // (m, g) holds rows 4g .. 4g + 3 of column m, so the rest is shared.
+#pragma unroll
+    for (int m = 0; m < kDotRows; ++m) {
+      dacc[m] += __shfl_xor(dacc[m], 16);
+      dacc[m] += __shfl_xor(dacc[m], 32);
+    }
+#pragma unroll
+    for (int m = 0; m < kDotRows; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = __shfl(dacc[m], g * 4 + r);
+        if (mcol == m) acc[r] = v;
+      }
+  }
 
   // The KS slices of each n-tile are added through LDS, in slice order, into
   // the slice-0 wavefront. The staged activations are dead by now, so their
@@ -623,7 +710,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   if (argmax) argmax_finish();
 }
 
-template <int FMT, int WAVES, int DEPTH, int EPI, int XP>
+template <int FMT, int WAVES, int DEPTH, int EPI, int XP, int DOT = 0>
 hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
                       float tensor_scale, void* y, float* val, void* workspace, int m, int64_t n, int64_t k,
                       hipStream_t stream) {
@@ -634,7 +721,7 @@ hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, c
   const unsigned grid = static_cast<unsigned>(whole + (groups - whole) * (p.split > 1 ? p.split : 0));
   // Dynamic LDS above the 64 KiB default must be allowed per kernel.
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH, EPI, XP>),
+      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH, EPI, XP, DOT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBudget));
   if (attr != hipSuccess) return attr;
   char* wsb = static_cast<char*>(workspace);
@@ -647,7 +734,7 @@ hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, c
     amax.idx = static_cast<int*>(y);
     amax.val = val;
   }
-  hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH, EPI, XP>), dim3(grid), dim3(WAVES * 64), p.lds_bytes, stream,
+  hipLaunchKernelGGL((gemm_kernel<FMT, WAVES, DEPTH, EPI, XP, DOT>), dim3(grid), dim3(WAVES * 64), p.lds_bytes, stream,
                      static_cast<const _Float16*>(x), static_cast<const uint8_t*>(packed), row_scales,
                      tensor_scale, y, ws, counters, amax, m, static_cast<int>(n),
                      static_cast<int>(k), NT, KU, p.units_per_split, p.lds_stride, p.k_slices, groups, whole,
@@ -662,6 +749,25 @@ template <int FMT, int WAVES, int DEPTH, int EPI>
 hipError_t launch_cfg_e(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
                         float tensor_scale, void* y, float* val, void* workspace, int m, int64_t n, int64_t k,
                         hipStream_t stream) {
+  if constexpr (EPI == kEpiNone && DEPTH <= 4) {
+    // The packed-dot path (full stage, plain epilogue, depths 2..4).
+    if (p.dot_rows && p.x_stage == kStageFull) {
+      switch (p.dot_rows) {
+        case 1:
+          return launch_kernel<FMT, WAVES, DEPTH, EPI, 0, 1>(p, x, packed, row_scales, tensor_scale, y, val,
+                                                             workspace, m, n, k, stream);
+        case 2:
+          return launch_kernel<FMT, WAVES, DEPTH, EPI, 0, 2>(p, x, packed, row_scales, tensor_scale, y, val,
+                                                             workspace, m, n, k, stream);
+        case 4:
+          return launch_kernel<FMT, WAVES, DEPTH, EPI, 0, 4>(p, x, packed, row_scales, tensor_scale, y, val,
+                                                             workspace, m, n, k, stream);
+        default:
+          return hipErrorInvalidValue;
+      }
+    }
+  }
+  if (p.dot_rows) return hipErrorInvalidValue;
   if (p.x_stage == kStageFull)
     return launch_kernel<FMT, WAVES, DEPTH, EPI, 0>(p, x, packed, row_scales, tensor_scale, y, val, workspace, m,
                                                     n, k, stream);
@@ -789,6 +895,9 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   if (o.epilogue == kEpiSwiglu && (waves / ks) % 2) return false;
   const int depth = w.depth ? w.depth : 3;
   if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
+  // The packed-dot path: the plain epilogue, a full stage, depths 2..4, and
+  // at most 4 rows (its cost grows with M; the MFMA's does not).
+  if (o.valu_dot && (o.epilogue != kEpiNone || depth > 4 || m > 4 || o.x_stage == kStageRing)) return false;
 
   // Groups kept whole (split > 1 only): a whole group's workgroup covers
   // all KU units, so a full stage must hold them.
@@ -803,9 +912,9 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   const bool full_ok = (split > 1 && whole > 0 ? KU : ups) <= max_ups;
   const bool ring_ok = depth <= 4 && ring_pieces(waves, ks, m) <= kRingMaxPieces &&
                        2 * static_cast<int64_t>(m) * k < (int64_t(1) << 31);
-  int stage = w.x_stage ? w.x_stage : (m >= kRingMinM ? kStageRing : kStageFull);
+  int stage = o.valu_dot ? kStageFull : w.x_stage ? w.x_stage : (m >= kRingMinM ? kStageRing : kStageFull);
   if (stage != kStageFull && stage != kStageRing) return false;
-  if (!o.x_stage) {
+  if (!o.x_stage && !o.valu_dot) {
     if (stage == kStageRing && !ring_ok) stage = kStageFull;
     if (stage == kStageFull && !full_ok) stage = kStageRing;
   }
@@ -816,6 +925,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   p->waves = waves;
   p->depth = depth;
   p->k_slices = ks;
+  p->dot_rows = o.valu_dot ? (m <= 1 ? 1 : m <= 2 ? 2 : 4) : 0;
   p->units_per_split = static_cast<int>(ups);
   p->lds_stride = static_cast<int>((split > 1 && whole > 0 ? KU : ups) * kUnitK + kRowPad);
   p->x_stage = stage;

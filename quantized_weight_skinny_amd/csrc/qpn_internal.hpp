@@ -18,6 +18,7 @@ struct LaunchOverride {
   int epilogue = 0;  // 0: y[M, N]; 1: SwiGLU (h[M, N/2]); 2: greedy argmax per row
   int x_stage = 0;   // 0 automatic; kStageFull; kStageRing
   int whole_groups = 0;  // with split > 1: leading n-tile groups kept whole (not split)
+  int valu_dot = 0;      // 1: the VALU packed-dot path instead of the MFMA
 };
 
 constexpr int kStageFull = 1;  // the workgroup's whole K range of x staged before the stream
@@ -27,6 +28,7 @@ struct GemmPlan {
   int split;
   int waves;
   int k_slices;    // wavefronts of a workgroup that split one n-tile's K range
+  int dot_rows;    // 0: MFMA; 1, 2 or 4: the VALU packed-dot path for up to that many rows
   int depth;       // units of the weight stream each wavefront keeps in flight
   int epilogue;    // 0 y[M, N]; 1 h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:]; 2 argmax of each row
   int x_stage;     // kStageFull or kStageRing

@@ -207,23 +207,25 @@ def requantize_fp8_to_nvfp4(codes8, row_scales):
     return codes, scales, s_t
 
 
-def _launch(split_k=0, waves=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE, x_stage=0, whole_groups=0):
-    if split_k or waves or depth or k_slices or epilogue or x_stage or whole_groups:
-        return make_launch(split_k, waves, depth, k_slices, epilogue, x_stage, whole_groups)
+def _launch(split_k=0, waves=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE, x_stage=0, whole_groups=0,
+            valu_dot=0):
+    if split_k or waves or depth or k_slices or epilogue or x_stage or whole_groups or valu_dot:
+        return make_launch(split_k, waves, depth, k_slices, epilogue, x_stage, whole_groups, valu_dot)
     return None
 
 
-def workspace_bytes(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, x_stage=0, whole_groups=0):
+def workspace_bytes(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, x_stage=0, whole_groups=0,
+                    valu_dot=0):
     launch = _launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_SWIGLU if swiglu else QPN_EPILOGUE_NONE, x_stage,
-                     whole_groups)
+                     whole_groups, valu_dot)
     d = pw.desc()
     return qpn_workspace_bytes_tuned(d, m, launch) if launch is not None else qpn_workspace_bytes(d, m)
 
 
 def new_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, device="cuda", x_stage=0,
-                  whole_groups=0):
+                  whole_groups=0, valu_dot=0):
     """A zeroed workspace for gemm(pw) with m rows (None when none is needed)."""
-    need = workspace_bytes(pw, m, split_k, waves, depth, k_slices, swiglu, x_stage, whole_groups)
+    need = workspace_bytes(pw, m, split_k, waves, depth, k_slices, swiglu, x_stage, whole_groups, valu_dot)
     return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
 
 
@@ -243,13 +245,16 @@ def _run(x, pw, out, workspace, launch, cols, dtype=torch.float16):
     return out
 
 
-def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0, whole_groups=0):
-    """y[m, n] = x[m, k] @ dequant(W)^T in fp16 through qpn_gemm.
+def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0, whole_groups=0,
+         valu_dot=0):
+    """y[m, n] = x[m, k] @ dequant(W)^T in fp16 through qpn_gemm (any shape
+    field set: qpn_gemm_tuned; valu_dot=1: the VALU packed-dot path).
 
     A workspace, when one is needed and not given, is allocated zeroed per
     call; pass one from new_workspace() to reuse it across calls."""
     return _run(x, pw, out, workspace,
-                _launch(split_k, waves, depth, k_slices, x_stage=x_stage, whole_groups=whole_groups), pw.n)
+                _launch(split_k, waves, depth, k_slices, x_stage=x_stage, whole_groups=whole_groups,
+                        valu_dot=valu_dot), pw.n)
 
 
 def gemm_f32(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0, whole_groups=0):

@@ -101,9 +101,8 @@ def _w(fmt=q.QPN_FMT_NVFP4, n=512, k=1024, packed=FAKE, rs=FAKE):
     return q.make_weight(fmt, n, k, packed, 1.0, rs)
 
 
-def _gemm(x, w, y, m, ws=None, wsb=0, split=0, waves=0, depth=0, k_slices=0, reserved=0, x_stage=0):
-    launch = q.make_launch(split, waves, depth, k_slices, x_stage=x_stage)
-    launch.reserved = reserved
+def _gemm(x, w, y, m, ws=None, wsb=0, split=0, waves=0, depth=0, k_slices=0, valu_dot=0, x_stage=0):
+    launch = q.make_launch(split, waves, depth, k_slices, x_stage=x_stage, valu_dot=valu_dot)
     return q.lib().qpn_gemm_tuned(x, ctypes.byref(w), y, m, ws, wsb, ctypes.byref(launch), None)
 
 
@@ -133,7 +132,8 @@ def test_gemm_rejects_bad_arguments_before_any_device_call():
     assert _gemm(FAKE, _w(), FAKE, 1, waves=5) == err
     assert _gemm(FAKE, _w(), FAKE, 1, depth=5) == err
     assert _gemm(FAKE, _w(), FAKE, 1, k_slices=3) == err
-    assert _gemm(FAKE, _w(), FAKE, 1, reserved=1) == err
+    assert _gemm(FAKE, _w(), FAKE, 1, valu_dot=2) == err
+    assert _gemm(FAKE, _w(), FAKE, 1, valu_dot=-1) == err
     assert _gemm(FAKE, _w(), FAKE, 1, x_stage=3) == err
     assert _gemm(FAKE, _w(), FAKE, 1, x_stage=-1) == err
     assert _gemm(FAKE, _w(), FAKE, 1, waves=4, k_slices=8) == q.QPN_ERR_UNSUPPORTED
@@ -245,6 +245,27 @@ def test_every_tabled_shape_resolves_to_a_valid_plan(fmt, shape):
             need = q.qpn_workspace_bytes_tuned(w, m, p)
             if p.split_k > 1:
                 assert need >= p.split_k * m * n * 4
+
+
+def test_valu_dot_plans_and_checks():
+    """The VALU packed-dot path: m <= 4, plain epilogue, full stage, depth
+    2..4; never chosen automatically."""
+    unsup = q.QPN_ERR_UNSUPPORTED
+    w = _w(n=34816, k=5120)
+    for m in range(1, 17):
+        assert _plan(w, m).valu_dot == 0
+    for m in (1, 2, 3, 4):
+        p = _plan(w, m, valu_dot=1)
+        assert p.valu_dot == 1 and p.x_stage == q.QPN_X_STAGE_FULL and p.depth <= 4
+    assert _plan(w, 5, valu_dot=1) == unsup
+    assert _plan(w, 1, valu_dot=1, x_stage=q.QPN_X_STAGE_RING) == unsup
+    assert _plan(w, 1, valu_dot=1, depth=6) == unsup
+    assert _plan(w, 1, valu_dot=1, epilogue=q.QPN_EPILOGUE_F32) == unsup
+    assert _plan(w, 1, valu_dot=1, epilogue=q.QPN_EPILOGUE_SWIGLU) == unsup
+    assert _plan(w, 1, valu_dot=1, epilogue=q.QPN_EPILOGUE_ARGMAX) == unsup
+    # a long K at m = 4 splits so that the full stage fits
+    p = _plan(_w(n=5120, k=17408), 4, valu_dot=1)
+    assert p.x_stage == q.QPN_X_STAGE_FULL and 2 * 4 * (-(-68 // p.split_k) * 256 + 8) <= 79 * 1024
 
 
 def test_whole_groups_plans():
