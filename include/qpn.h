@@ -315,8 +315,12 @@ qpn_status qpn_gemm_f32(const void* x_dev, const qpn_weight* w, float* y_dev, in
  *   launch    NULL or a launch shape (its epilogue field 0 or
  *             QPN_EPILOGUE_ARGMAX); other arguments as in qpn_gemm_tuned.
  * The workspace is always needed: qpn_workspace_bytes_tuned(w, m, launch)
- * with launch->epilogue = QPN_EPILOGUE_ARGMAX. Its counters must be zero
- * before the first call, and every call leaves them zero.
+ * with launch->epilogue = QPN_EPILOGUE_ARGMAX. It holds 64 x 16 key slots
+ * (8 KiB) besides any split-K counters; all must be zero before the first
+ * call, and every call leaves them zero. The call enqueues two kernels: the
+ * GEMM, whose workgroups fold their best (logit, index) keys into the slots
+ * with device-scope atomic max, and a one-workgroup kernel that reads the
+ * slots, writes idx and val, and clears them.
  * (The pages speak of a native 4-bit lm_head; folding the greedy argmax into
  * it is a reading of how a verify step uses that head.)
  */

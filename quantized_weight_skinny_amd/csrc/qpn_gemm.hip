@@ -109,9 +109,12 @@ constexpr int kMinSliceUnits = 4;
 constexpr int kRingMinM = 5;
 constexpr int kEpiNone = 0, kEpiSwiglu = 1, kEpiArgmax = 2, kEpiF32 = 3;  // GemmPlan::epilogue
 // The argmax epilogue's arrival counters in the workspace's control block.
+// The argmax epilogue's key slots in the workspace's control block: group g
+// folds its best key of row m into slot (g % kArgmaxSubs, m) with a
+// device-scope atomic max, so thousands of groups spread over 64 addresses
+// per row.
 constexpr int kArgmaxSubs = 64;
-constexpr int kCounterStride = 16;  // ints: one 64-byte line per counter
-constexpr size_t kControlBytes = (kArgmaxSubs + 1) * kCounterStride * sizeof(int) + 192;  // padded to 256
+constexpr size_t kControlBytes = static_cast<size_t>(kArgmaxSubs) * kMaxM * sizeof(unsigned long long);
 constexpr int kFixupBatch = 8;  // split-K partials loaded together by the last workgroup
 
 constexpr int kRowPad = 8;          // fp16 pad per staged row (bank spread)
@@ -265,8 +268,7 @@ __device__ __forceinline__ void unit_dot(const Unit<kFmtFp8>& w, const _Float16*
 
 // Outputs of the greedy-argmax epilogue and its workspace.
 struct ArgmaxOut {
-  unsigned long long* keys;  // [groups][M]: each group's best key per row
-  int* done;                 // arrival counters: kArgmaxSubs, kCounterStride ints apart, then the total
+  unsigned long long* keys;  // [kArgmaxSubs][kMaxM] key slots (zero between calls)
   int* idx;                  // [M] int32 argmax
   float* val;                // [M] fp32 max logit, or null
 };
@@ -572,57 +574,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     return;
   }
   // Greedy argmax: every row's best key over this group's logits (LDS
-  // atomics, order-free), stored for the group; the last group to finish
-  // reduces all groups' keys.
+  // atomics, order-free), folded into the group's key slot with a
+  // device-scope atomic max that nothing waits for. Max is order-free, so
+  // the slots hold the same keys whatever order the groups run in;
+  // argmax_decode_kernel, launched next on the stream, reads and clears them.
   auto argmax_finish = [&]() {
     __syncthreads();
     if (tid < M)
-      __hip_atomic_store(amax.keys + static_cast<size_t>(grp) * M + tid, best[tid], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // Arrival in two levels, so that thousands of groups do not queue on one
-    // counter: group g counts on sub-counter g % kArgmaxSubs (each on its own
-    // cache line); the last of each sub-counter's groups counts on the total.
-    if (tid == 0) {
-      const int sub = grp % kArgmaxSubs;
-      const int members = (groups - 1 - sub) / kArgmaxSubs + 1;
-      int* sc = amax.done + sub * kCounterStride;
-      int last = __hip_atomic_fetch_add(sc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1;
-      if (last) {
-        __hip_atomic_store(sc, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        int* top = amax.done + kArgmaxSubs * kCounterStride;
-        const int subs = groups < kArgmaxSubs ? groups : kArgmaxSubs;
-        last = __hip_atomic_fetch_add(top, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == subs - 1;
-        if (last) __hip_atomic_store(top, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      last_group = last;
-    }
-    if (tid < M) best[tid] = 0;
-    __syncthreads();
-    if (!last_group) return;
-    const int total = groups * M;
-    for (int i0 = tid; i0 < total; i0 += WAVES * 64 * kFixupBatch) {
-      unsigned long long part[kFixupBatch];
-#pragma unroll
-      for (int j = 0; j < kFixupBatch; ++j) {
-        const int i = i0 + j * WAVES * 64;
-        part[j] = i < total ? __hip_atomic_load(amax.keys + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-      }
-#pragma unroll
-      for (int j = 0; j < kFixupBatch; ++j) {
-        const int i = i0 + j * WAVES * 64;
-        if (i < total) __hip_atomic_fetch_max(&best[i % M], part[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-    }
-    __syncthreads();
-    if (tid < M) {
-      int n;
-      float v;
-      argmax_decode(best[tid], &n, &v);
-      amax.idx[tid] = n;
-      if (amax.val) amax.val[tid] = v;
-    }
+      __hip_atomic_fetch_max(amax.keys + (grp % kArgmaxSubs) * kMaxM + tid, best[tid], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   };
   if (argmax) {
     if (tid < M) best[tid] = 0;
@@ -711,6 +671,33 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   if (argmax) argmax_finish();
 }
 
+// After the argmax GEMM on the same stream: thread (m, sub) reads and clears
+// key slot (sub, m) (device-scope loads and stores: the slots were written by
+// device-scope atomics from every XCD); the largest key of each row gives
+// its index and value.
+__global__ __launch_bounds__(kArgmaxSubs* kMaxM) void argmax_decode_kernel(unsigned long long* keys, int M,
+                                                                          int* idx, float* val) {
+  __shared__ unsigned long long best[kMaxM];
+  const int t = threadIdx.x;
+  if (t < M) best[t] = 0;
+  __syncthreads();
+  const int m = t / kArgmaxSubs, sub = t % kArgmaxSubs;
+  if (m < M) {
+    unsigned long long* slot = keys + sub * kMaxM + m;
+    const unsigned long long k = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_max(&best[m], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __syncthreads();
+  if (t < M) {
+    int n;
+    float v;
+    argmax_decode(best[t], &n, &v);
+    idx[t] = n;
+    if (val) val[t] = v;
+  }
+}
+
 template <int FMT, int WAVES, int DEPTH, int EPI, int XP, int DOT = 0>
 hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, const float* row_scales,
                       float tensor_scale, void* y, float* val, void* workspace, int m, int64_t n, int64_t k,
@@ -728,10 +715,9 @@ hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, c
   char* wsb = static_cast<char*>(workspace);
   int* counters = p.split > 1 ? reinterpret_cast<int*>(wsb) : nullptr;
   float* ws = p.split > 1 ? reinterpret_cast<float*>(wsb + p.partials_offset) : nullptr;
-  ArgmaxOut amax{nullptr, nullptr, nullptr, nullptr};
+  ArgmaxOut amax{nullptr, nullptr, nullptr};
   if (EPI == kEpiArgmax) {
-    amax.keys = reinterpret_cast<unsigned long long*>(wsb + p.keys_offset);
-    amax.done = reinterpret_cast<int*>(wsb + p.control_offset);
+    amax.keys = reinterpret_cast<unsigned long long*>(wsb + p.control_offset);
     amax.idx = static_cast<int*>(y);
     amax.val = val;
   }
@@ -740,6 +726,12 @@ hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, c
                      tensor_scale, y, ws, counters, amax, m, static_cast<int>(n),
                      static_cast<int>(k), NT, KU, p.units_per_split, p.lds_stride, p.k_slices, groups, whole,
                      p.split);
+  if constexpr (EPI == kEpiArgmax) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(argmax_decode_kernel, dim3(1), dim3(kArgmaxSubs * kMaxM), 0, stream, amax.keys, m,
+                       amax.idx, amax.val);
+  }
   return hipGetLastError();
 }
 
@@ -834,19 +826,11 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   const int64_t max_ups = (static_cast<int64_t>(kLdsBudget) / (2 * m) - kRowPad) / kUnitK;
   if (max_ups < 1) return false;
 
-  // A tuned launch for this shape fills in what the caller left automatic.
-  // The argmax epilogue ends every workgroup with a publication and a count,
-  // so it prefers few, wide groups: 8 n-tiles a workgroup, no K slices, depth
-  // 2 (measured on the 151936-row head: 72 us at M = 1 against 80 us with
-  // the plain GEMM's shape).
+  // A tuned launch for this shape fills in what the caller left automatic
+  // (the argmax epilogue takes the plain GEMM's shape: on the 151936-row
+  // head it measured the same as few, wide groups, 70.2 against 70.4 us at
+  // M = 1 and 70.1 against 70.2 at M = 8).
   LaunchOverride w = o;
-  if (o.epilogue == kEpiArgmax) {
-    if (!w.waves && !w.k_slices) {
-      w.waves = 8;
-      w.k_slices = 1;
-    }
-    if (!w.depth) w.depth = 2;
-  }
   if (const TunedLaunch* t = find_tuned(fmt, n, k, m)) {
     if (!w.split) w.split = t->split;
     if (!w.waves) w.waves = t->waves;
@@ -943,16 +927,12 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   const size_t counters = (static_cast<size_t>(NT) * sizeof(int) + 255) & ~size_t(255);
   p->control_offset = counters;
   p->partials_offset = counters + kControlBytes;
-  p->keys_offset = p->partials_offset;
   p->workspace_bytes = 0;
-  if (split > 1) {
-    p->keys_offset += (static_cast<size_t>(split) * m * n * sizeof(float) + 255) & ~size_t(255);
-    p->workspace_bytes = p->keys_offset;
-  }
-  if (o.epilogue == kEpiArgmax) {
-    const size_t groups = static_cast<size_t>(ceil_div(NT, waves / ks));
-    p->workspace_bytes = p->keys_offset + groups * m * sizeof(unsigned long long);
-  }
+  if (split > 1)
+    p->workspace_bytes =
+        p->partials_offset + ((static_cast<size_t>(split) * m * n * sizeof(float) + 255) & ~size_t(255));
+  if (o.epilogue == kEpiArgmax && p->workspace_bytes < p->partials_offset)
+    p->workspace_bytes = p->partials_offset;  // the key slots of the control block
   return true;
 }
 

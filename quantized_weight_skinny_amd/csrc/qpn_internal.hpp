@@ -37,13 +37,11 @@ struct GemmPlan {
   int lds_stride;  // halves per staged activation row (full stage)
   size_t lds_bytes;
   // Workspace: one split-K arrival counter per n-tile (padded to 256 bytes),
-  // a control block (the argmax epilogue's arrival counters), fp32 partials
-  // [split][m][n] from partials_offset (split > 1), then the argmax
-  // epilogue's per-group keys [groups][m] from keys_offset. 0 bytes when
-  // neither split-K nor the argmax epilogue needs it.
+  // a control block (the argmax epilogue's 64 x 16 key slots, 8 KiB), then
+  // fp32 partials [split][m][n] from partials_offset (split > 1). 0 bytes
+  // when neither split-K nor the argmax epilogue needs it.
   size_t control_offset;
   size_t partials_offset;
-  size_t keys_offset;
   size_t workspace_bytes;
 };
 

@@ -94,7 +94,7 @@ def test_tensor_scale_helper():
 
 
 # the workspace's control block: 64 + 1 arrival counters on 64-byte lines, padded
-CONTROL = 65 * 64 + 192
+CONTROL = 64 * 16 * 8  # the control block: 64 x 16 argmax key slots
 
 
 def _w(fmt=q.QPN_FMT_NVFP4, n=512, k=1024, packed=FAKE, rs=FAKE):
@@ -391,10 +391,11 @@ def test_argmax_epilogue_checks_and_workspace():
     w = _w(n=151936, k=5120)
     p = q.qpn_gemm_plan(w, 1, am)
     assert p.epilogue == q.QPN_EPILOGUE_ARGMAX
-    groups = -(-(151936 // 16) // (p.waves_per_group // p.k_slices))
     need = q.qpn_workspace_bytes_tuned(w, 1, am)
-    # counters, control block, then one 8-byte key per group and row
-    assert need == (151936 // 16 * 4 + 255) // 256 * 256 + CONTROL + groups * 8
+    # n-tile counters, then the control block of key slots (no split here)
+    assert p.split_k == 1
+    assert need == (151936 // 16 * 4 + 255) // 256 * 256 + CONTROL
+    assert q.qpn_workspace_bytes_tuned(w, 16, am) == need
     idx, val = FAKE, FAKE + 64
     call = q.lib().qpn_gemm_argmax
     assert call(FAKE, ctypes.byref(w), idx, val, 1, None, 0, None, None) == q.QPN_ERR_INVALID_ARG

@@ -76,4 +76,4 @@ def test_graph_replay_fused_epilogues(split):
         assert np.array_equal(to_host(idx), eager[1]), i
         assert np.array_equal(to_host(val).view(np.uint32), eager[2].view(np.uint32)), i
     # 128 n-tile counters (512 B) and the control block are back at zero
-    assert not to_host(ws_a[:512 + 65 * 64 + 192]).any()
+    assert not to_host(ws_a[:512 + 64 * 16 * 8]).any()
