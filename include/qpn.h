@@ -166,11 +166,13 @@ qpn_status qpn_requantize_fp8_nvfp4(const uint8_t* fp8_codes_dev, const float* r
 
 /* Device workspace qpn_gemm needs for this weight and row count (0 if none).
  * When K is split over several workgroups the workspace holds one arrival
- * counter per n-tile and fp32 partial sums. The counters sit at offsets that
- * depend only on the weight, so one workspace (sized for the largest m)
- * serves calls with any m and epilogue. They must be zero before the first
- * call that uses the workspace (allocate it zeroed); every call leaves them
- * zero again. Calls that run at the same time must not share a workspace. */
+ * counter per n-tile, an 8 KiB control block (the key slots of
+ * qpn_gemm_argmax) and fp32 partial sums. The counters and the control block
+ * sit at offsets that depend only on the weight, so one workspace (sized for
+ * the largest m) serves calls with any m and epilogue. They must be zero
+ * before the first call that uses the workspace (allocate it zeroed); every
+ * call leaves them zero again. Calls that run at the same time must not
+ * share a workspace. */
 size_t qpn_workspace_bytes(const qpn_weight* w, int32_t m);
 
 /*
