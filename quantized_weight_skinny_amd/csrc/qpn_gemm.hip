@@ -108,7 +108,6 @@ const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
 constexpr int kMinSliceUnits = 4;
 constexpr int kRingMinM = 5;
 constexpr int kEpiNone = 0, kEpiSwiglu = 1, kEpiArgmax = 2, kEpiF32 = 3;  // GemmPlan::epilogue
-// The argmax epilogue's arrival counters in the workspace's control block.
 // The argmax epilogue's key slots in the workspace's control block: group g
 // folds its best key of row m into slot (g % kArgmaxSubs, m) with a
 // device-scope atomic max, so thousands of groups spread over 64 addresses

@@ -93,8 +93,8 @@ def test_tensor_scale_helper():
     assert q.qpn_nvfp4_tensor_scale(0.0) == 1.0
 
 
-# the workspace's control block: 64 + 1 arrival counters on 64-byte lines, padded
-CONTROL = 64 * 16 * 8  # the control block: 64 x 16 argmax key slots
+# the workspace's control block: 64 x 16 argmax key slots of 8 bytes
+CONTROL = 64 * 16 * 8
 
 
 def _w(fmt=q.QPN_FMT_NVFP4, n=512, k=1024, packed=FAKE, rs=FAKE):

@@ -42,8 +42,8 @@ def test_graph_replay_matches_eager(fmt, n, k, m):
 @pytest.mark.parametrize("split", [0, 3])
 def test_graph_replay_fused_epilogues(split):
     """The SwiGLU and greedy-argmax epilogues captured together in one graph
-    (the argmax's arrival counters and the split-K counters are left at zero by
-    each call, so every replay reproduces the eager bits)."""
+    (the argmax's key slots and the split-K counters are left at zero by each
+    call, so every replay reproduces the eager bits)."""
     say("graph replay epilogues", split)
     n, k, m = 2048, 2304, 5
     w = workloads.weights(n, k, 41)
