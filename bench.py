@@ -8,13 +8,23 @@ enough distinct copies (>= 2 GiB) that no launch finds its matrix in the
 
 Prints one JSON line. ``value`` is the effective HBM read bandwidth of the
 step (algorithmic bytes: packed codes + block scales + x + y, divided by the
-step time). Also reported: the read-only streaming ceiling measured in the
-same run (on a 4 GiB buffer and at the size of each large matrix), per-matrix
-times for every workload (NVFP4 M=1 and M=8, FP8 M=1,2,4, the GEMV case, the
-per-GPU shapes of 4-way tensor parallelism, the 16-row verify block), the
-full 64-layer decode step as stream-ordered launches and as one HIP graph,
-the roofline of the dominant kernel, and the CPU oracle timed on a bounded
-sample (baseline only). ``--quick`` keeps only the headline step.
+step time); the timed steps follow at least SETTLE_MS of untimed replays of
+the same step, back to back, so they run at settled clocks. Also reported:
+
+* plain reads: the read-only kernel swept over grid x loads in flight for a
+  4 GiB buffer (the measured ceiling), for one launch the size of the whole
+  step, for each timed matrix's size, and for the step's two matrices as two
+  back-to-back launches (the launch-for-launch floor of the step);
+* per-matrix times for every workload (NVFP4 M=1, 8, 16; FP8 M=1, 2, 4, 8;
+  the GEMV case; the per-GPU shapes of 4-way tensor parallelism; the output
+  head, plain and with the greedy argmax), each against the same-size read;
+* the full 64-layer decode step as stream-ordered launches and as one graph;
+* the roofline of the dominant kernel;
+* the CPU oracle (cpu_baseline leg): timed on sampled rows of every timed
+  configuration (dequantize + matmul, and matmul alone), and used there to
+  check the GPU's outputs for the same rows and activations.
+
+``--quick`` keeps only the reads of the step's sizes and the headline step.
 """
 
 import argparse
@@ -75,7 +85,6 @@ def parse():
     p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--quick", action="store_true", help="only the headline step (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=1024, help="rows per matrix in the CPU oracle sample")
     p.add_argument("--launches", default="",
                    help="profiling mode: comma-separated fmt:matrix:m[:full|ring|dot] cases (dot: the VALU "
                         "packed-dot path, full stage), each launched --steps times in order (after one warm-up "
@@ -124,7 +133,13 @@ class Mat:
         self.name, self.fmt = name, fmt
         n, k = workloads.SHAPES[name]
         self.n, self.k = n, k
+        self.wl = wl
         w = workloads.weights(n, k, workloads.seed_for(wl, name, "W"))
+        # host copies the cpu_baseline leg needs: the sampled rows and the
+        # tensor-wide amax (a plain max of the generated input)
+        self.sample = sample_rows(n)
+        self.w_rows = np.ascontiguousarray(w[self.sample])
+        self.amax = float(np.abs(w).max())
         wd = torch.from_numpy(w).to("cuda")
         del w
         if fmt == "nvfp4":
@@ -147,6 +162,33 @@ class Mat:
     def bytes_for(self, m, swiglu=False, argmax=False):
         out = 8 * m if argmax else 2 * m * (self.n // 2 if swiglu else self.n)
         return self.weight_bytes + 2 * m * self.k + out
+
+
+def sample_rows(n):
+    """Output rows the bench checks per configuration: the first and last 64,
+    128 spread over N and 64 in the last eighth (where a balanced launch puts
+    its split-K tail groups)."""
+    rows = set(range(min(64, n))) | set(range(max(0, n - 64), n))
+    rows |= set(np.linspace(0, n - 1, 128).astype(int).tolist())
+    rows |= set(np.linspace(n - n // 8, n - 1, 64).astype(int).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+CHECKS = []
+
+
+def gpu_sample(mat, m, label):
+    """One launch of the timed plan on seeded activations; the sampled output
+    columns are kept for the cpu_baseline leg, which computes the same rows
+    with the oracle and compares (outside every timed region)."""
+    import torch
+    from quantized_weight_skinny_amd import torch_api as qt
+    x = workloads.activations(m, mat.k, workloads.seed_for(mat.wl, mat.name, f"x{m}"))
+    y = qt.gemm(torch.from_numpy(x).to("cuda"), mat.copies[0])
+    torch.cuda.synchronize()
+    CHECKS.append({"label": label, "fmt": mat.fmt, "name": mat.name, "n": mat.n, "k": mat.k, "m": m,
+                   "rows": mat.sample, "w_rows": mat.w_rows, "amax": mat.amax, "x": x,
+                   "y": y.cpu().numpy()[:, mat.sample].astype(np.float64)})
 
 
 def capture(launches):
@@ -271,60 +313,77 @@ def time_mlp(gate_up, down, m, reps=10):
     return us, nbytes / (us * 1e-6) / 1e9
 
 
-def read_ceiling(nbytes=4 << 30, reps=6):
-    """Best read-only streaming bandwidth over a sweep of grid sizes (GB/s)."""
+READ_GRIDS = (256, 512, 768, 1024, 1536, 2048, 3072, 4096)
+READ_LOADS = (2, 4, 8)
+
+
+def _read_graph_us(buf, size, grid, loads, reps):
+    """µs per launch of the read kernel over `size`-byte slices of `buf`
+    (rotating, a graph of back-to-back launches), settled clocks, median of
+    `reps` replays."""
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
-    from quantized_weight_skinny_amd import qpn_read_ceiling_grid
-    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    cus = qpn_read_ceiling_grid() // 8
-    best = (0.0, 0)
-    for grid in (cus, cus * 2, cus * 3, cus * 4, cus * 6, cus * 8):
-        sink = torch.empty(grid * 4, dtype=torch.int32, device="cuda")
-        qt.read_ceiling(buf, grid, sink)
-        torch.cuda.synchronize()
-        s = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        settle(lambda: qt.read_ceiling(buf, grid, sink))
-        e0.record(s)
-        for _ in range(reps):
-            qt.read_ceiling(buf, grid, sink)
-        e1.record(s)
-        torch.cuda.synchronize()
-        gbps = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        if gbps > best[0]:
-            best = (gbps, grid)
+    nsl = max(1, min(64, buf.numel() // size))
+    slices = [buf[i * size:(i + 1) * size] for i in range(nsl)]
+    sink = torch.empty(grid * 4, dtype=torch.int32, device="cuda")
+    launches = [(lambda sl=sl: qt.read_ceiling(sl, grid, sink, loads)) for sl in slices]
+    for fn in launches:
+        fn()
+    g = capture(launches)
+    us = replay_us(g, len(launches), reps)
+    del g
+    return us
+
+
+def read_sweep(sizes, total=4 << 30, reps=5):
+    """The best plain read a single launch of each size can make: the read
+    kernel over rotating slices of a `total`-byte buffer, swept over
+    READ_GRIDS x READ_LOADS (loads in flight per thread), settled clocks.
+    Returns {name: {"bytes", "us", "GBps", "grid", "loads"}} (GB/s = bytes per
+    launch / µs per launch, the launch gap of a graph replay included)."""
+    import torch
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, nbytes in sizes.items():
+        size = min(total, (int(nbytes) + 255) // 256 * 256)
+        best = None
+        for grid in READ_GRIDS:
+            for loads in READ_LOADS:
+                us = _read_graph_us(buf, size, grid, loads, reps)
+                if best is None or us < best[0]:
+                    best = (us, grid, loads)
+        out[name] = {"bytes": size, "us": round(best[0], 3), "GBps": round(size / (best[0] * 1e-6) / 1e9, 1),
+                     "grid": best[1], "loads": best[2]}
+        log(f"read {name} ({size / 1e6:.1f} MB): {best[0]:.2f} us, {out[name]['GBps']:.0f} GB/s "
+            f"(grid {best[1]}, {best[2]} loads)")
     del buf
     torch.cuda.empty_cache()
-    return best
+    return out
 
 
-def read_ceiling_sized(nbytes, total=4 << 30, reps=2):
-    """Read-kernel bandwidth when each launch reads one matrix-sized slice of
-    a large buffer (rotating slices, graph of back-to-back launches)."""
+def read_pair_us(a, b, total=4 << 30, reps=5):
+    """µs per pair of back-to-back plain reads of the sizes and launch shapes
+    a and b (two entries of read_sweep): the launch-for-launch floor of a
+    two-GEMM step."""
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
-    from quantized_weight_skinny_amd import qpn_read_ceiling_grid
     buf = torch.empty(total, dtype=torch.uint8, device="cuda")
-    size = (nbytes + 15) // 16 * 16
-    slices = [buf[i * size:(i + 1) * size] for i in range(total // size)]
-    grid = qpn_read_ceiling_grid() // 4
-    sink = torch.empty(grid * 4, dtype=torch.int32, device="cuda")
-    g = capture([(lambda sl=sl: qt.read_ceiling(sl, grid, sink)) for sl in slices])
-    g.replay()
-    torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    settle(g.replay)
-    e0.record(s)
-    for _ in range(reps):
-        g.replay()
-    e1.record(s)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * len(slices))
+    span = a["bytes"] + b["bytes"]
+    npair = max(1, min(32, total // span))
+    sink = torch.empty(4096 * 4, dtype=torch.int32, device="cuda")
+    launches = []
+    for i in range(npair):
+        base = i * span
+        sa, sb = buf[base:base + a["bytes"]], buf[base + a["bytes"]:base + span]
+        launches.append(lambda sa=sa, sb=sb: (qt.read_ceiling(sa, a["grid"], sink, a["loads"]),
+                                              qt.read_ceiling(sb, b["grid"], sink, b["loads"])))
+    for fn in launches:
+        fn()
+    g = capture(launches)
+    us = replay_us(g, len(launches), reps)
     del g, buf
     torch.cuda.empty_cache()
-    return size / (us * 1e-6) / 1e9
+    return us
 
 
 KERNEL_SOURCES = ("qpn_device.hpp", "qpn_gemm.hip", "qpn_internal.hpp")
@@ -439,39 +498,89 @@ def decode_step(ms=(1, 2, 4, 8), reps=3):
     return out
 
 
-def cpu_baseline(rows):
-    """The oracle (numpy, float64 dequantize then matmul) on a bounded sample:
-    the first ``rows`` rows of gate_up and of down at M=1, repeated to about
-    10 s of CPU time. GB/s over the same algorithmic bytes as the GPU step."""
+def cpu_baseline(min_s=0.3):
+    """The oracle as it stands (numpy: float64 dequantize, then float64
+    matmul) on the bench's sampled rows of every timed configuration: the
+    oracle quantizes the sampled rows of W itself (untimed; NVFP4 with the
+    tensor scale of the whole matrix's amax), then dequantize + matmul and
+    matmul alone are timed (repeated for at least ``min_s`` each), and the
+    GPU's outputs for the same rows and activations are checked against the
+    result (|y_gpu - y| <= 2e-3 sum|wx| + 1e-3). GB/s count the sample's
+    algorithmic bytes. The 64-layer decode step at M=1 is composed from the
+    per-matrix rates (64 x per layer + lm_head)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = 1
-    parts = []
-    for name in ("gate_up", "down"):
-        n, k = workloads.SHAPES[name]
-        w = workloads.weights(n, k, workloads.seed_for("nvfp4_27b_m1", name, "W"), rows=slice(0, rows))
-        full_amax = None  # the sample is quantized on its own; timing does not depend on values
-        codes, sc, s_t = oracle.quantize_nvfp4(w, full_amax)
-        x = workloads.activations(1, k, workloads.seed_for("nvfp4_27b_m1", name, "x"))
-        nbytes = rows * k // 2 + rows * k // 16 + 2 * k + 2 * rows
-        parts.append((codes, sc, s_t, x, nbytes))
-    total_bytes = 0
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        for codes, sc, s_t, x, nbytes in parts:
-            oracle.gemm_nvfp4(x, codes, sc, s_t)
-            total_bytes += nbytes
-        reps += 1
-        if time.perf_counter() - t0 > 10.0:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": total_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows} rows of gate_up and of down (NVFP4, M=1), numpy float64 dequantize + "
-                      f"matmul, {reps} passes in {dt:.1f} s"}
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    rows_out, checks_ok = [], True
+    rate = {}
+    for c in CHECKS:
+        w, m, n, k = c["w_rows"], c["m"], c["n"], c["k"]
+        r = len(c["rows"])
+        if c["fmt"] == "nvfp4":
+            codes, sc, s_t = oracle.quantize_nvfp4(w, oracle.nvfp4_tensor_scale(c["amax"]))
+            row_bytes = k // 2 + k // 16
+            deq = lambda: oracle.dequantize_nvfp4(codes, sc, s_t)  # noqa: E731
+        else:
+            codes, rs = oracle.quantize_fp8(w)
+            row_bytes = k + 4
+            deq = lambda: oracle.dequantize_fp8(codes, rs)  # noqa: E731
+        x = c["x"].astype(np.float64)
+        t0, reps = time.perf_counter(), 0
+        while True:
+            wdq = deq()
+            y_ref = x @ wdq.T
+            reps += 1
+            if time.perf_counter() - t0 >= min_s:
+                break
+        t_total = (time.perf_counter() - t0) / reps
+        t0, reps2 = time.perf_counter(), 0
+        while True:
+            y_ref = x @ wdq.T
+            reps2 += 1
+            if time.perf_counter() - t0 >= min_s:
+                break
+        t_mm = (time.perf_counter() - t0) / reps2
+        b = np.abs(x) @ np.abs(wdq).T
+        tol = 2e-3 * b + 1e-3
+        excess = float(np.max(np.abs(c["y"] - y_ref) / tol))
+        ok = bool(excess <= 1.0)
+        checks_ok &= ok
+        nbytes = r * row_bytes + 2 * m * k + 2 * m * r
+        per_row_s = t_total / r
+        rate[(c["fmt"], c["name"], m)] = (per_row_s, row_bytes)
+        rows_out.append({"config": c["label"], "rows": r, "total_s": round(t_total, 5), "matmul_s": round(t_mm, 6),
+                         "GBps": round(nbytes / t_total / 1e9, 4), "matmul_only_GBps": round(nbytes / t_mm / 1e9, 4),
+                         "gpu_check": "pass" if ok else "FAIL", "max_err_over_bound": round(excess, 4)})
+        log(f"cpu {c['label']}: {r} rows, {nbytes / t_total / 1e9:.3f} GB/s (matmul only {nbytes / t_mm / 1e9:.2f}); "
+            f"gpu check {'pass' if ok else 'FAIL'} (max err / bound {excess:.3f})")
+    # the headline workload (gate_up + down at M = 1) as one rate
+    head = [row for row in rows_out if row["config"] in ("nvfp4_m1/gate_up", "nvfp4_m1/down")]
+    value = None
+    if head:
+        tot_b = sum(row["GBps"] * row["total_s"] * 1e9 for row in head)
+        value = tot_b / sum(row["total_s"] for row in head) / 1e9
+    composed = None
+    need = [("fp8", "qkv", 1), ("fp8", "o_proj", 1), ("nvfp4", "gate_up", 1), ("nvfp4", "down", 1),
+            ("nvfp4", "lm_head", 1)]
+    if all(key in rate for key in need):
+        t_layer = sum(rate[key][0] * workloads.SHAPES[key[1]][0] for key in need[:4])
+        t_head = rate[need[4]][0] * workloads.SHAPES["lm_head"][0]
+        t_step = workloads.DECODE_LAYERS * t_layer + t_head
+        step_bytes = sum(rate[key][1] * workloads.SHAPES[key[1]][0] for key in need[:4]) * workloads.DECODE_LAYERS \
+            + rate[need[4]][1] * workloads.SHAPES["lm_head"][0]
+        composed = {"m": 1, "s_per_step": round(t_step, 3), "weight_GBps": round(step_bytes / t_step / 1e9, 4),
+                    "kind": "composed: 64 x (qkv FP8 + o_proj FP8 + gate_up NVFP4 + down NVFP4) + lm_head NVFP4, "
+                            "each from its sampled-row rate scaled to all rows"}
+    return {"value": round(value, 4) if value is not None else None, "unit": "GB/s", "cores": cores,
+            "blas_threads": blas_threads, "kind": "oracle",
+            "sample": f"{len(CHECKS)} configurations, the bench's sampled output rows of each (first/last 64, 128 "
+                      "spread, 64 in the last eighth of N), all M activation rows; numpy float64 dequantize + matmul; "
+                      "value = gate_up + down at M=1",
+            "gpu_checks": "pass" if checks_ok else "FAIL", "rows": rows_out, "decode_step_27b_composed": composed}
 
 
 def main():
@@ -485,15 +594,24 @@ def main():
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
+    import quantized_weight_skinny_amd as q
     from quantized_weight_skinny_amd import torch_api as qt  # noqa: F401  (fails loudly without libqpn.so)
     if args.launches:
         run_launches(args.launches, args.steps)
         return
 
-    log("read ceiling")
-    with mark("read_ceiling/4GiB"):
-        ceiling, ceiling_grid = read_ceiling()
-    log(f"ceiling {ceiling:.0f} GB/s (grid {ceiling_grid})")
+    nv = lambda name: q.qpn_packed_bytes(q.QPN_FMT_NVFP4, *workloads.SHAPES[name])  # noqa: E731
+    f8 = lambda name: q.qpn_packed_bytes(q.QPN_FMT_FP8_E4M3, *workloads.SHAPES[name]) + 4 * workloads.SHAPES[name][0]  # noqa: E731,E501
+    sizes = {"ceiling_4GiB": 4 << 30, "step": nv("gate_up") + nv("down"), "gate_up": nv("gate_up"), "down": nv("down")}
+    if not args.quick:
+        sizes.update({"qkv_nvfp4": nv("qkv"), "o_proj_nvfp4": nv("o_proj"), "qkv_fp8": f8("qkv"),
+                      "o_proj_fp8": f8("o_proj"), "down_fp8": f8("down"), "lm_head": nv("lm_head")})
+    log("plain reads (grid x loads sweep per size)")
+    with mark("read_sweep"):
+        reads = read_sweep(sizes)
+    ceiling = reads["ceiling_4GiB"]["GBps"]
+    pair_us = read_pair_us(reads["gate_up"], reads["down"])
+    log(f"ceiling {ceiling:.0f} GB/s; gate_up + down as two plain reads: {pair_us:.2f} us a pair")
 
     log("building rotating weights for the M=1 MLP step")
     wl = "nvfp4_27b_m1"
@@ -515,11 +633,9 @@ def main():
         qt.gemm(x2, down.copies[i % r_steps], out=y, workspace=ws_d)
 
     # One HIP graph holds one cycle of steps (every rotating copy once); the W
-    # warmup steps and the K timed steps are back-to-back replays of it, plus
-    # a graph of the leftover steps when W or K is not a whole number of
-    # cycles. Small graphs replayed back to back keep the GPU streaming with
-    # no idle; one graph of thousands of launches does not. The cycle graph
-    # is checked against the eager step first.
+    # warmup steps, the settling replays and the K timed steps are replays of
+    # it, plus a graph of the leftover steps when W or K is not a whole number
+    # of cycles. The cycle graph is checked against the eager step first.
     for i in range(r_steps):
         step(i)
     torch.cuda.synchronize()
@@ -543,6 +659,12 @@ def main():
     with mark("step/warmup"):
         run_steps(args.warmup)
     torch.cuda.synchronize()
+    # After the synchronize the GPU is idle, and an idle GPU restarts the
+    # clock transient of a streaming load; untimed replays of the same step
+    # (at least SETTLE_MS of GPU time) run back to back before the timed ones,
+    # so the timed steps see the same settled clocks as every other row.
+    settle_t0 = time.perf_counter()
+    settle(cycle.replay)
     wall0 = time.perf_counter()
     with mark("step/timed"):
         t0.record(s)
@@ -553,6 +675,7 @@ def main():
     ms_step = t0.elapsed_time(t1) / args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
     del cycle, leftover
+    log(f"settle enqueued in {1e3 * (wall0 - settle_t0):.1f} ms of host time")
 
     # The dominant kernel (gate_up): a graph of back-to-back launches over
     # the rotating copies, events on the launch stream around it.
@@ -561,21 +684,16 @@ def main():
     log(f"step {ms_step * 1e3:.1f} us, {value:.0f} GB/s; gate_up {gate_up_us:.1f} us per launch, "
         f"{achieved:.0f} GB/s; wall {wall:.3f} s; traffic {traffic}")
 
-    # Same-size ceiling: the read kernel over 100 MB slices of a rotating
-    # buffer, the size of one gate_up launch.
-    same_size = read_ceiling_sized(gate_up.weight_bytes)
-    log(f"read ceiling at gate_up size: {same_size:.0f} GB/s")
-
-    extras, same_size_ceilings = {}, {"gate_up": round(same_size, 1)}
+    extras = {}
     decode = None
+    same_size = {"gate_up": "gate_up", "gate_up_swiglu": "gate_up", "down": "down"}
     if not args.quick:
         per = {}
-        per["nvfp4_m1/gate_up"] = time_matrix(gate_up, 1)
-        per["nvfp4_m1/down"] = time_matrix(down, 1)
-        per["nvfp4_m8/gate_up"] = time_matrix(gate_up, 8)
-        per["nvfp4_m8/down"] = time_matrix(down, 8)
-        per["nvfp4_m16/gate_up"] = time_matrix(gate_up, 16)
-        per["nvfp4_m16/down"] = time_matrix(down, 16)
+        for mm in (1, 8, 16):
+            per[f"nvfp4_m{mm}/gate_up"] = time_matrix(gate_up, mm)
+            gpu_sample(gate_up, mm, f"nvfp4_m{mm}/gate_up")
+            per[f"nvfp4_m{mm}/down"] = time_matrix(down, mm)
+            gpu_sample(down, mm, f"nvfp4_m{mm}/down")
         for mm in (1, 8):
             per[f"nvfp4_m{mm}/gate_up_swiglu"] = time_matrix(gate_up, mm, swiglu=True)
             per[f"nvfp4_m{mm}/mlp_swiglu"] = time_mlp(gate_up, down, mm)
@@ -583,50 +701,48 @@ def main():
         torch.cuda.empty_cache()
         for name in ("qkv", "o_proj"):
             mat = Mat(name, "nvfp4", "nvfp4_27b_m8")
-            per[f"nvfp4_m8/{name}"] = time_matrix(mat, 8)
+            for mm in (1, 8):
+                per[f"nvfp4_m{mm}/{name}"] = time_matrix(mat, mm)
+                gpu_sample(mat, mm, f"nvfp4_m{mm}/{name}")
             del mat
             torch.cuda.empty_cache()
         for name in ("qkv", "down", "o_proj"):
             mat = Mat(name, "fp8", "fp8_27b_m124")
-            for mm in (1, 2, 4):
+            for mm in (1, 2, 4, 8):
                 per[f"fp8_m{mm}/{name}"] = time_matrix(mat, mm)
+                gpu_sample(mat, mm, f"fp8_m{mm}/{name}")
             del mat
             torch.cuda.empty_cache()
         mat = Mat("gemv", "nvfp4", "nvfp4_gemv_m1")
         per["nvfp4_m1/gemv"] = time_matrix(mat, 1)
+        gpu_sample(mat, 1, "nvfp4_m1/gemv")
         del mat
         for name in ("qkv_tp4", "o_proj_tp4", "gate_up_tp4", "down_tp4"):
             mat = Mat(name, "nvfp4", "nvfp4_27b_tp4")
             for mm in (1, 8):
                 per[f"nvfp4_m{mm}/{name}"] = time_matrix(mat, mm)
+                gpu_sample(mat, mm, f"nvfp4_m{mm}/{name}")
             del mat
             torch.cuda.empty_cache()
         head = Mat("lm_head", "nvfp4", "decode_step_27b", copies=6)
-        per["nvfp4_m1/lm_head"] = time_matrix(head, 1)
-        per["nvfp4_m8/lm_head"] = time_matrix(head, 8)
-        per["nvfp4_m1/lm_head_argmax"] = time_matrix(head, 1, argmax=True)
-        per["nvfp4_m8/lm_head_argmax"] = time_matrix(head, 8, argmax=True)
+        for mm in (1, 8):
+            per[f"nvfp4_m{mm}/lm_head"] = time_matrix(head, mm)
+            gpu_sample(head, mm, f"nvfp4_m{mm}/lm_head")
+            per[f"nvfp4_m{mm}/lm_head_argmax"] = time_matrix(head, mm, argmax=True)
         del head
         torch.cuda.empty_cache()
+        same_size.update({"qkv": "qkv_nvfp4", "o_proj": "o_proj_nvfp4", "lm_head": "lm_head",
+                          "lm_head_argmax": "lm_head"})
+        same_size_f8 = {"qkv": "qkv_fp8", "o_proj": "o_proj_fp8", "down": "down_fp8"}
         for key, (us, gbps) in per.items():
-            extras[key] = {"us": round(us, 2), "GBps": round(gbps, 1),
-                           "frac_of_measured_ceiling": round(gbps / ceiling, 4)}
-            log(f"{key}: {us:.1f} us {gbps:.0f} GB/s ({100 * gbps / ceiling:.1f}% of ceiling)")
-        # the read kernel at the size of the other large matrices, for
-        # comparing each GEMM with a plain read of its own size
-        for name, fmt in (("down", "nvfp4"), ("qkv", "fp8"), ("o_proj", "nvfp4")):
-            n, k = workloads.SHAPES[name]
-            nbytes = n * k // 2 + n * k // 16 if fmt == "nvfp4" else n * k + 4 * n
-            same_size_ceilings[f"{name}_{fmt}"] = round(read_ceiling_sized(nbytes), 1)
-            log(f"read ceiling at {name} {fmt} size ({nbytes / 1e6:.1f} MB): "
-                f"{same_size_ceilings[f'{name}_{fmt}']:.0f} GB/s")
-        same_of = {"gate_up": "gate_up", "gate_up_swiglu": "gate_up", "down": "down_nvfp4", "o_proj": "o_proj_nvfp4"}
-        for key, row in extras.items():
+            row = {"us": round(us, 2), "GBps": round(gbps, 1), "frac_of_measured_ceiling": round(gbps / ceiling, 4)}
             fmt_m, name = key.split("/")
-            ref = "qkv_fp8" if (fmt_m.startswith("fp8") and name == "qkv") else \
-                (same_of.get(name) if fmt_m.startswith("nvfp4") else None)
-            if ref in same_size_ceilings:
-                row["frac_of_same_size_read"] = round(row["GBps"] / same_size_ceilings[ref], 4)
+            ref = (same_size_f8 if fmt_m.startswith("fp8") else same_size).get(name)
+            if ref in reads:
+                row["same_size_read_us"] = reads[ref]["us"]
+                row["frac_of_same_size_read"] = round(reads[ref]["us"] / us, 4)
+            extras[key] = row
+            log(f"{key}: {us:.1f} us {gbps:.0f} GB/s ({100 * gbps / ceiling:.1f}% of ceiling)")
         decode = {str(m): {"ms_per_step": round(v[0], 4), "GBps": round(v[1], 1),
                            "weight_and_io_bytes": v[2], "frac_of_measured_ceiling": round(v[1] / ceiling, 4),
                            "stream_ordered_ms_per_step": round(v[3], 4),
@@ -635,9 +751,16 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        cpu = cpu_baseline(args.cpu_rows)
-        log(f"cpu baseline {cpu['value']:.3f} GB/s")
+        if not CHECKS:
+            gate_up = Mat("gate_up", "nvfp4", wl, copies=1)
+            gpu_sample(gate_up, 1, "nvfp4_m1/gate_up")
+            del gate_up
+            down = Mat("down", "nvfp4", wl, copies=1)
+            gpu_sample(down, 1, "nvfp4_m1/down")
+            del down
+        log("cpu baseline (oracle) and the check of every timed configuration")
+        cpu = cpu_baseline()
+        log(f"cpu baseline {cpu['value']} GB/s; gpu checks {cpu['gpu_checks']}")
 
     try:
         sha = subprocess.run(["git", "rev-parse", "--short", "HEAD"], capture_output=True, text=True,
@@ -658,15 +781,18 @@ def main():
         "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": "nvfp4_27b_m1: NVFP4 gate_up 34816x5120 + down 5120x17408, M=1",
-                   "m": 1, "format": "nvfp4", "rotating_copies": r_steps, "step_bytes": step_bytes},
+                   "m": 1, "format": "nvfp4", "rotating_copies": r_steps, "step_bytes": step_bytes,
+                   "settle_ms": SETTLE_MS},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "kernel": "gemm_kernel<NVFP4> on gate_up 34816x5120, M=1",
                      "launch_us": round(gate_up_us, 3), "algorithmic_bytes": gate_up_bytes},
-        "measured_read_ceiling_GBps": round(ceiling, 1),
-        "read_ceiling_at_gate_up_size_GBps": round(same_size, 1),
-        "read_ceiling_same_size_GBps": same_size_ceilings,
+        "measured_read_ceiling_GBps": ceiling,
         "frac_of_measured_ceiling": round(value / ceiling, 4),
+        "plain_reads": reads,
+        "step_as_two_plain_reads_us": round(pair_us, 3),
+        "frac_of_two_plain_reads": round(pair_us / (ms_step * 1e3), 4),
+        "frac_of_step_sized_read": round(reads["step"]["us"] / (ms_step * 1e3), 4),
         "cpu_baseline": cpu,
         "per_matrix": extras,
         "decode_step_27b": decode,

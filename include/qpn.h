@@ -12,7 +12,8 @@
  *   - All pointers named *_dev are device pointers (hipMalloc'd, or torch CUDA
  *     tensors); the caller owns every buffer. The library allocates no memory.
  *   - `stream` is a hipStream_t (NULL = the default stream). Device work is
- *     enqueued on it and the call returns without waiting, unless stated.
+ *     enqueued on it and the call returns without waiting, unless stated (the
+ *     two pack calls wait for their stream: they report invalid codes).
  *   - Arguments are validated on the host before any HIP call; a failed check
  *     returns a negative qpn_status and enqueues nothing. A failed kernel
  *     launch returns QPN_ERR_HIP. Faults inside kernels surface
@@ -34,7 +35,7 @@ typedef enum {
   QPN_OK = 0,
   QPN_ERR_INVALID_ARG = -1,      /* null / misaligned pointer, bad size or format */
   QPN_ERR_UNSUPPORTED = -2,      /* valid request the library does not implement */
-  QPN_ERR_BAD_CODE = -3,         /* reserved: invalid codes are counted, see pack */
+  QPN_ERR_BAD_CODE = -3,         /* pack met invalid E4M3 codes (NaN, sign-set block scale) */
   QPN_ERR_BUFFER_TOO_SMALL = -4, /* packed buffer or workspace below the required size */
   QPN_ERR_HIP = -5               /* a HIP runtime call failed */
 } qpn_status;
@@ -87,13 +88,18 @@ size_t qpn_packed_bytes(int32_t format, int64_t n, int64_t k);
  *                    consecutive elements of a row along k.
  *   packed_dev       output, packed_bytes >= qpn_packed_bytes(NVFP4, n, k),
  *                    16-byte aligned. Every byte of the packed form is written.
- *   bad_codes_dev    NULL, or a device int32 to which the kernel adds the
- *                    number of invalid block-scale codes it found: NaN (0x7F,
- *                    0xFF) or sign-set (0x80..0xFF; NVFP4 block scales are
- *                    positive). The caller zeroes it first and checks it after
- *                    the stream is synchronized. Such scales are packed as
- *                    they are and only give wrong (NaN or negated) outputs
- *                    for their block; they never make the GEMM fault.
+ *   bad_codes_dev    a device int32 (4-byte aligned, not NULL) that the call
+ *                    uses as its counter: it is cleared, the pack kernels add
+ *                    the invalid block-scale codes they find, NaN (0x7F, 0xFF)
+ *                    or sign-set (0x80..0xFF: NVFP4 block scales are
+ *                    positive), and it holds that count when the call returns.
+ * Validation: the call waits for `stream` (pack is an offline, once-per-weight
+ * step; do not capture it in a graph) and returns QPN_ERR_BAD_CODE if any
+ * invalid code was found. The packed buffer is written all the same, byte for
+ * byte (unpack reads it back), but must not be handed to a GEMM: a NaN or
+ * negative scale would turn its block's outputs NaN or negate them (it never
+ * makes the GEMM fault). Nothing to pack (n == 0 or k == 0): QPN_OK, the
+ * counter is not touched.
  * The pages keep published FP4 regions in their own format rather than
  * converting them ([P3] "v1.0 got us here. v1.1 removes its last
  * compromise."); this entry point takes such codes as they are.
@@ -103,8 +109,9 @@ qpn_status qpn_pack_nvfp4(const uint8_t* codes_dev, const uint8_t* block_scales_
                           int32_t* bad_codes_dev, void* stream);
 
 /* Canonical FP8 -> packed layout. codes_dev: uint8 [n][k] row-major E4M3FN
- * codes. bad_codes_dev as for qpn_pack_nvfp4, counting the NaN codes 0x7F
- * and 0xFF (weights of either sign are valid).
+ * codes. bad_codes_dev and the validation as for qpn_pack_nvfp4 (the call
+ * waits for its stream and returns QPN_ERR_BAD_CODE), counting the NaN codes
+ * 0x7F and 0xFF (weights of either sign are valid).
  * The per-row fp32 scales stay in a separate caller-owned array. ([P3] "v1.0
  * got us here. v1.1 removes its last compromise.": FP8 regions keep FP8.) */
 qpn_status qpn_pack_fp8(const uint8_t* codes_dev, int64_t n, int64_t k,
@@ -233,8 +240,17 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *                    QPN_ERR_UNSUPPORTED). It exists to measure the MFMA
  *                    choice against; qpn_gemm never picks it. Other values
  *                    return QPN_ERR_INVALID_ARG.
- * The result bits depend on split_k, whole_groups, k_slices and valu_dot
- * (the summation order), not on the other fields.
+ *   block_columns    one activation row (m == 1) of NVFP4 weights with a full
+ *                    stage: 1 on (QPN_ERR_UNSUPPORTED where not possible),
+ *                    0 (automatic) and 2 off; qpn_gemm never picks it. The
+ *                    matrix cores' 16 output columns then carry the 16
+ *                    K-blocks of each 256-element unit instead of activation
+ *                    rows (the B operand is the activation row laid out
+ *                    block-diagonally), so each E4M3 block scale multiplies
+ *                    one fp32 block sum per weight row instead of every
+ *                    decoded weight. Other values return QPN_ERR_INVALID_ARG.
+ * The result bits depend on split_k, whole_groups, k_slices, valu_dot and
+ * block_columns (the summation order), not on the other fields.
  */
 typedef enum {
   QPN_EPILOGUE_NONE = 0,
@@ -253,6 +269,7 @@ typedef struct {
   int32_t x_stage;
   int32_t whole_groups;
   int32_t valu_dot;
+  int32_t block_columns;
 } qpn_launch;
 
 /* qpn_gemm with an explicit launch shape (NULL = automatic). A shape that
@@ -333,12 +350,14 @@ qpn_status qpn_gemm_argmax(const void* x_dev, const qpn_weight* w, int32_t* idx_
  * Read-only streaming kernel that measures the HBM read ceiling the GEMM is
  * compared against ([P3] "What I actually built": bandwidth is quoted against
  * a measured read-only ceiling). Reads `bytes` (a multiple of 16) from buf_dev
- * with 16-byte loads on `grid` workgroups of 256 threads (grid 0 = automatic;
- * qpn_read_ceiling_grid() gives that count) and writes one word per
- * wavefront to sink_dev (uint32 [4 * grid]).
+ * with 16-byte non-temporal loads, grid-stride, on `grid` workgroups of 256
+ * threads (grid 0 = automatic; qpn_read_ceiling_grid() gives that count),
+ * `loads` loads in flight per thread (2, 4 or 8; 0 = 4), and writes one
+ * word per wavefront to sink_dev (uint32 [4 * grid]). A sweep over grid and
+ * loads gives the best plain read a launch of that size can make.
  */
 qpn_status qpn_read_ceiling(const void* buf_dev, size_t bytes, uint32_t* sink_dev,
-                            int32_t grid, void* stream);
+                            int32_t grid, int32_t loads, void* stream);
 int32_t qpn_read_ceiling_grid(void);
 
 #ifdef __cplusplus

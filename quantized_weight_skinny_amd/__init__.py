@@ -53,6 +53,7 @@ class qpn_launch(ctypes.Structure):
         ("x_stage", ctypes.c_int32),
         ("whole_groups", ctypes.c_int32),
         ("valu_dot", ctypes.c_int32),
+        ("block_columns", ctypes.c_int32),
     ]
 
 
@@ -98,7 +99,7 @@ SIGNATURES = {
     "qpn_gemm_swiglu": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
     "qpn_gemm_f32": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
     "qpn_gemm_argmax": (_I32, [_P, _W, _P, _P, _I32, _P, _SZ, _L, _P]),
-    "qpn_read_ceiling": (_I32, [_P, _SZ, _P, _I32, _P]),
+    "qpn_read_ceiling": (_I32, [_P, _SZ, _P, _I32, _I32, _P]),
     "qpn_read_ceiling_grid": (_I32, []),
 }
 
@@ -188,8 +189,9 @@ def qpn_workspace_bytes(weight, m):
 
 
 def make_launch(split_k=0, waves_per_group=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE,
-                x_stage=QPN_X_STAGE_AUTO, whole_groups=0, valu_dot=0):
-    return qpn_launch(split_k, waves_per_group, depth, k_slices, epilogue, x_stage, whole_groups, valu_dot)
+                x_stage=QPN_X_STAGE_AUTO, whole_groups=0, valu_dot=0, block_columns=0):
+    return qpn_launch(split_k, waves_per_group, depth, k_slices, epilogue, x_stage, whole_groups, valu_dot,
+                      block_columns)
 
 
 def qpn_workspace_bytes_tuned(weight, m, launch):
@@ -231,8 +233,8 @@ def qpn_gemm_argmax(x, weight, idx, val, m, workspace, workspace_bytes, launch, 
                   "qpn_gemm_argmax")
 
 
-def qpn_read_ceiling(buf, nbytes, sink, grid, stream):
-    return _check(lib().qpn_read_ceiling(buf, nbytes, sink, grid, stream), "qpn_read_ceiling")
+def qpn_read_ceiling(buf, nbytes, sink, grid, loads, stream):
+    return _check(lib().qpn_read_ceiling(buf, nbytes, sink, grid, loads, stream), "qpn_read_ceiling")
 
 
 def qpn_read_ceiling_grid():

@@ -56,6 +56,28 @@ size_t qpn_packed_bytes(int32_t format, int64_t n, int64_t k) {
   return 0;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Pack's validation: the counter is cleared, the pack kernels add the invalid
+// codes they meet, and the count is read back after the stream has drained,
+// so the call reports them itself (QPN_ERR_BAD_CODE) and a GEMM is never
+// handed a weight with them.
+template <typename Launch>
+qpn_status pack_checked(int32_t* bad_codes_dev, hipStream_t s, Launch launch) {
+  if (hipMemsetAsync(bad_codes_dev, 0, sizeof(int32_t), s) != hipSuccess) return QPN_ERR_HIP;
+  if (launch() != hipSuccess) return QPN_ERR_HIP;
+  int32_t bad = 0;
+  if (hipMemcpyAsync(&bad, bad_codes_dev, sizeof bad, hipMemcpyDeviceToHost, s) != hipSuccess) return QPN_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return QPN_ERR_HIP;
+  return bad ? QPN_ERR_BAD_CODE : QPN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 qpn_status qpn_pack_nvfp4(const uint8_t* codes_dev, const uint8_t* block_scales_dev, int64_t n,
                           int64_t k, void* packed_dev, size_t packed_bytes, int32_t* bad_codes_dev,
                           void* stream) {
@@ -64,10 +86,12 @@ qpn_status qpn_pack_nvfp4(const uint8_t* codes_dev, const uint8_t* block_scales_
   if (need == 0) return QPN_OK;
   if (!codes_dev || !block_scales_dev || !packed_dev || !aligned(packed_dev, 16))
     return QPN_ERR_INVALID_ARG;
-  if (bad_codes_dev && !aligned(bad_codes_dev, 4)) return QPN_ERR_INVALID_ARG;
+  if (!bad_codes_dev || !aligned(bad_codes_dev, 4)) return QPN_ERR_INVALID_ARG;
   if (packed_bytes < need) return QPN_ERR_BUFFER_TOO_SMALL;
-  return from_hip(qpn::launch_pack_nvfp4(codes_dev, block_scales_dev, n, k, packed_dev,
-                                         bad_codes_dev, as_stream(stream)));
+  const hipStream_t s = as_stream(stream);
+  return pack_checked(bad_codes_dev, s, [&] {
+    return qpn::launch_pack_nvfp4(codes_dev, block_scales_dev, n, k, packed_dev, bad_codes_dev, s);
+  });
 }
 
 qpn_status qpn_pack_fp8(const uint8_t* codes_dev, int64_t n, int64_t k, void* packed_dev,
@@ -76,9 +100,11 @@ qpn_status qpn_pack_fp8(const uint8_t* codes_dev, int64_t n, int64_t k, void* pa
   const size_t need = qpn_packed_bytes(QPN_FMT_FP8_E4M3, n, k);
   if (need == 0) return QPN_OK;
   if (!codes_dev || !packed_dev || !aligned(packed_dev, 16)) return QPN_ERR_INVALID_ARG;
-  if (bad_codes_dev && !aligned(bad_codes_dev, 4)) return QPN_ERR_INVALID_ARG;
+  if (!bad_codes_dev || !aligned(bad_codes_dev, 4)) return QPN_ERR_INVALID_ARG;
   if (packed_bytes < need) return QPN_ERR_BUFFER_TOO_SMALL;
-  return from_hip(qpn::launch_pack_fp8(codes_dev, n, k, packed_dev, bad_codes_dev, as_stream(stream)));
+  const hipStream_t s = as_stream(stream);
+  return pack_checked(bad_codes_dev, s,
+                      [&] { return qpn::launch_pack_fp8(codes_dev, n, k, packed_dev, bad_codes_dev, s); });
 }
 
 qpn_status qpn_unpack_nvfp4(const void* packed_dev, size_t packed_bytes, int64_t n, int64_t k,
@@ -156,6 +182,7 @@ namespace {
 bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   if (!l) return true;
   if ((l->valu_dot != 0 && l->valu_dot != 1) || l->whole_groups < 0) return false;
+  if (l->block_columns < 0 || l->block_columns > 2) return false;
   if (l->x_stage != QPN_X_STAGE_AUTO && l->x_stage != QPN_X_STAGE_FULL && l->x_stage != QPN_X_STAGE_RING)
     return false;
   if (l->split_k < 0 || l->waves_per_group < 0 || l->depth < 0 || l->k_slices < 0) return false;
@@ -170,6 +197,7 @@ bool to_override(const qpn_launch* l, qpn::LaunchOverride* o) {
   o->x_stage = l->x_stage;
   o->whole_groups = l->whole_groups;
   o->valu_dot = l->valu_dot;
+  o->block_cols = l->block_columns;
   return true;
 }
 
@@ -204,6 +232,7 @@ qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launc
   resolved->x_stage = p.x_stage;
   resolved->whole_groups = p.whole_groups;
   resolved->valu_dot = p.dot_rows ? 1 : 0;
+  resolved->block_columns = p.block_cols ? 1 : 2;
   return QPN_OK;
 }
 
@@ -289,13 +318,13 @@ qpn_status qpn_gemm_f32(const void* x_dev, const qpn_weight* w, float* y_dev, in
 
 int32_t qpn_read_ceiling_grid(void) { return qpn::read_ceiling_default_grid(); }
 
-qpn_status qpn_read_ceiling(const void* buf_dev, size_t bytes, uint32_t* sink_dev, int32_t grid,
+qpn_status qpn_read_ceiling(const void* buf_dev, size_t bytes, uint32_t* sink_dev, int32_t grid, int32_t loads,
                             void* stream) {
-  if (!buf_dev || !sink_dev || !aligned(buf_dev, 16) || bytes % 16 || grid < 0)
-    return QPN_ERR_INVALID_ARG;
+  if (!buf_dev || !sink_dev || !aligned(buf_dev, 16) || bytes % 16 || grid < 0) return QPN_ERR_INVALID_ARG;
+  if (loads != 0 && loads != 2 && loads != 4 && loads != 8) return QPN_ERR_INVALID_ARG;
   if (bytes == 0) return QPN_OK;
   const int g = grid ? grid : qpn::read_ceiling_default_grid();
-  return from_hip(qpn::launch_read_ceiling(buf_dev, bytes, sink_dev, g, as_stream(stream)));
+  return from_hip(qpn::launch_read_ceiling(buf_dev, bytes, sink_dev, g, loads ? loads : 4, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -108,6 +108,8 @@ const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
 constexpr int kMinSliceUnits = 4;
 constexpr int kRingMinM = 5;
 constexpr int kEpiNone = 0, kEpiSwiglu = 1, kEpiArgmax = 2, kEpiF32 = 3;  // GemmPlan::epilogue
+// DOT template value of the block-column path (one activation row, NVFP4, full stage).
+constexpr int kDotBlockCols = -1;
 // The argmax epilogue's key slots in the workspace's control block: group g
 // folds its best key of row m into slot (g % kArgmaxSubs, m) with a
 // device-scope atomic max, so thousands of groups spread over 64 addresses
@@ -143,6 +145,14 @@ __device__ __forceinline__ void lds_dma16(const void* src, _Float16* lds_dst) {
 }
 
 __device__ __forceinline__ h8 x_fragment(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
+
+// LDS pointers kept as such (a select between two of them as generic pointers
+// would become flat loads, which also wait on the vector-memory counter).
+typedef const __attribute__((address_space(3))) _Float16* lds_half_ptr;
+__device__ __forceinline__ lds_half_ptr to_lds(const _Float16* p) { return (lds_half_ptr)(p); }
+__device__ __forceinline__ h8 x_fragment(lds_half_ptr p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) h8*>(p);
+}
 
 // silu(g) = g / (1 + e^-g) in fp32 (e^-g overflows to +inf for g < -88,
 // giving -0, the limit).
@@ -197,6 +207,44 @@ __device__ __forceinline__ void unit_mfma(const Unit<kFmtNvfp4>& w, const _Float
     const h8 b = x_fragment(xrow + t * 8);
     acc[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t & 1], 0, 0, 0);
   }
+}
+
+// Block columns (one activation row, NVFP4): the MFMA's 16 output columns
+// carry the unit's 16 K-blocks instead of 16 activation rows. The B operand
+// is block-diagonal: at step t, lane (j = lane % 16, g = lane / 16) holds the
+// 8 activations of its K group g only if j is the block those 8 elements
+// belong to (j == 4g + t/2), and zeros otherwise, so output column j
+// accumulates the unit's block j alone: P[r][j] = sum over block j of
+// E2M1(w[r][k]) * x[k]. Each block scale then multiplies one fp32 block sum
+// per row, 4 per lane and unit, instead of every decoded weight pair (the
+// decode is only the fp4 -> fp16 conversion). bp[p] is the lane's x pointer
+// for steps 2p, 2p+1: its own x where j - 4g == p, else a zero region that
+// the same offsets keep inside. Output lane (j, g) needs the block scales
+// S[4g + i][j], i = 0..3, which the packed layout holds in lane
+// (4g + i) + 16 * (j / 4), byte j % 4 (sbase is that lane's byte address for
+// i = 0; ssel picks byte j % 4 of two dwords into the low two bytes).
+__device__ __forceinline__ void unit_block_cols(const Unit<kFmtNvfp4>& w, const lds_half_ptr (&bp)[4], int off,
+                                                int sbase, uint32_t ssel, f4& acc) {
+  const uint32_t d0 = __builtin_amdgcn_ds_bpermute(sbase, static_cast<int>(w.sc));
+  const uint32_t d1 = __builtin_amdgcn_ds_bpermute(sbase + 4, static_cast<int>(w.sc));
+  const uint32_t d2 = __builtin_amdgcn_ds_bpermute(sbase + 8, static_cast<int>(w.sc));
+  const uint32_t d3 = __builtin_amdgcn_ds_bpermute(sbase + 12, static_cast<int>(w.sc));
+  const uint32_t s4 = __builtin_amdgcn_perm(d1, d0, ssel) | (__builtin_amdgcn_perm(d3, d2, ssel) << 16);
+  const f2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s4, 1.0f, false);
+  const f2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s4, 1.0f, true);
+  f4 d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t c = word(t < 4 ? w.c0 : w.c1, t & 3);
+    const h8 a = cat(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1),
+                     __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3));
+    const h8 b = x_fragment(bp[t >> 1] + off + t * 8);
+    d[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, d[t & 1], 0, 0, 0);
+  }
+  acc[0] = fmaf(s01.x, d[0][0], fmaf(s01.x, d[1][0], acc[0]));
+  acc[1] = fmaf(s01.y, d[0][1], fmaf(s01.y, d[1][1], acc[1]));
+  acc[2] = fmaf(s23.x, d[0][2], fmaf(s23.x, d[1][2], acc[2]));
+  acc[3] = fmaf(s23.y, d[0][3], fmaf(s23.y, d[1][3], acc[3]));
 }
 
 __device__ __forceinline__ void unit_mfma(const Unit<kFmtFp8>& w, const _Float16* xrow, f4 (&acc)[2]) {
@@ -349,7 +397,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
   const int mcol = lane & 15;
   const int g = lane >> 4;
   f4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  static_assert(DOT == 0 || (XP == 0 && EPI == kEpiNone), "packed-dot path: full stage, plain epilogue");
+  static_assert(DOT <= 0 || (XP == 0 && EPI == kEpiNone), "packed-dot path: full stage, plain epilogue");
+  static_assert(DOT != kDotBlockCols || (XP == 0 && FMT == kFmtNvfp4), "block columns: NVFP4, full stage");
   constexpr int kDotRows = DOT > 0 ? DOT : 1;
   float dacc[kDotRows];
 #pragma unroll
@@ -382,6 +431,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
             make_uint4(0u, 0u, 0u, 0u);
       }
     }
+    if constexpr (DOT == kDotBlockCols) {
+      // the zero region the block-column B operand reads where a lane holds no block
+      constexpr int kZeroChunks = (DEPTH * kUnitK + 64) / 8;
+      for (int idx = tid; idx < kZeroChunks; idx += WAVES * 64)
+        *reinterpret_cast<uint4*>(xs + M * stride + idx * 8) = make_uint4(0u, 0u, 0u, 0u);
+    }
     const int windows = (live_chunks + 63) / 64;
     for (int wi = wave; wi < M * windows; wi += WAVES) {
       const int m = wi / windows;
@@ -411,7 +466,39 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     const _Float16* xr[kDotRows];
 #pragma unroll
     for (int m = 0; m < kDotRows; ++m) xr[m] = xs + min(m, M - 1) * stride + g * 64 + wu0 * kUnitK;
-    if (active) {
+    if constexpr (DOT == kDotBlockCols) {
+      if (active) {
+        // Block columns (M = 1): lane (j, g) reads x for steps 2p, 2p+1 where
+        // j - 4g == p, and the zero region otherwise; only the x pointers
+        // advance with the stream, so every offset of an iteration stays
+        // inside the zero region.
+        const int j = lane & 15;
+        lds_half_ptr bp[4];
+        int inc[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const bool mine = j - 4 * g == p;
+          bp[p] = mine ? to_lds(xs + g * 64 + wu0 * kUnitK) : to_lds(xs + M * stride);
+          inc[p] = mine ? DEPTH * kUnitK : 0;
+        }
+        const int sbase = (4 * g + 16 * (j >> 2)) * 4;
+        const uint32_t ssel = static_cast<uint32_t>(j & 3) | (static_cast<uint32_t>(4 + (j & 3)) << 8) | 0x0C0C0000u;
+        f4 sacc = {0.f, 0.f, 0.f, 0.f};
+        for (int base = 0; base < wnu; base += DEPTH) {
+#pragma unroll
+          for (int i = 0; i < DEPTH; ++i) {
+            if (base + i < wnu) {
+              if constexpr (FMT == kFmtNvfp4) unit_block_cols(buf[i], bp, i * kUnitK, sbase, ssel, sacc);
+            }
+            load_unit(buf[i], stream, base + DEPTH + i, lane);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int p = 0; p < 4; ++p) bp[p] += inc[p];
+        }
+        acc2[0] = sacc;
+      }
+    } else if (active) {
       // Each slot of buf is consumed and then refilled in place (unit u +
       // DEPTH goes where unit u was), so the loop carries no register copies
       // and keeps DEPTH-1 units in flight while it computes.
@@ -509,6 +596,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_kernel(
     }
   }
   f4 acc = acc2[0] + acc2[1];
+  if constexpr (DOT == kDotBlockCols) {
+    // Add the 16 block columns of each row (lanes of one K group, j = lane %
+    // 16): every lane of the group ends with its rows' sums, so lane (0, g)
+    // holds rows 4g .. 4g + 3 of activation row 0, the MFMA output layout the
+    // rest of the kernel uses.
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) acc[r] += __shfl_xor(acc[r], o);
+  }
   if constexpr (DOT > 0) {
     // Packed-dot path: add the four K groups' sums of each row (lanes 16
     // apart), then move them to the MFMA's output layout, where lane
@@ -760,6 +857,12 @@ hipError_t launch_cfg_e(const GemmPlan& p, const void* x, const void* packed, co
     }
   }
   if (p.dot_rows) return hipErrorInvalidValue;
+  if (p.block_cols) {
+    if constexpr (FMT == kFmtNvfp4)
+      return launch_kernel<FMT, WAVES, DEPTH, EPI, 0, kDotBlockCols>(p, x, packed, row_scales, tensor_scale, y, val,
+                                                                     workspace, m, n, k, stream);
+    return hipErrorInvalidValue;
+  }
   if (p.x_stage == kStageFull)
     return launch_kernel<FMT, WAVES, DEPTH, EPI, 0>(p, x, packed, row_scales, tensor_scale, y, val, workspace, m,
                                                     n, k, stream);
@@ -903,6 +1006,19 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
     if (stage == kStageFull && !full_ok) stage = kStageRing;
   }
   if (stage == kStageFull ? !full_ok : !ring_ok) return false;
+  // Block columns: one activation row of NVFP4 weights, full stage, the MFMA
+  // path; 1 demands it, 0 and 2 leave it off. Its decode skips the
+  // per-weight scale multiply (45 instead of 66 VALU per unit), yet measured
+  // 2-5% slower as a standalone launch (11.2 against 11.0 us on down at one
+  // row, 18.2 against 17.9 on gate_up): the launch is bound by memory latency
+  // and balance, not by the VALU, and the path adds four LDS permutes a unit.
+  if (o.block_cols < 0 || o.block_cols > 2) return false;
+  const int64_t staged = (split > 1 && whole > 0 ? KU : ups) * kUnitK + kRowPad;  // halves per staged row
+  const bool bc_ok = m == 1 && fmt == kFmtNvfp4 && stage == kStageFull && !o.valu_dot &&
+                     (staged + depth * kUnitK + 64) * static_cast<int64_t>(sizeof(_Float16)) <=
+                         static_cast<int64_t>(kLdsBudget);
+  if (o.block_cols == 1 && !bc_ok) return false;
+  p->block_cols = bc_ok && o.block_cols == 1 ? 1 : 0;
 
   p->split = static_cast<int>(split);
   p->whole_groups = split > 1 ? static_cast<int>(whole) : 0;
@@ -915,6 +1031,8 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   p->x_stage = stage;
   p->lds_bytes = stage == kStageFull ? static_cast<size_t>(m) * p->lds_stride * sizeof(_Float16)
                                      : static_cast<size_t>(ks) * kRingSlots * m * kRingRow * sizeof(_Float16);
+  // ... plus the zero region the block-column B operand reads (DEPTH units and a chunk of slack)
+  if (p->block_cols) p->lds_bytes += static_cast<size_t>(depth * kUnitK + 64) * sizeof(_Float16);
   // K slices reduce through the same LDS: one 16x16 fp32 tile per wavefront.
   const size_t red_bytes = ks > 1 ? static_cast<size_t>(waves) * 64 * sizeof(f4) : 0;
   if (p->lds_bytes < red_bytes) p->lds_bytes = red_bytes;

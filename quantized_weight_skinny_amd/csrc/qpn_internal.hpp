@@ -19,6 +19,7 @@ struct LaunchOverride {
   int x_stage = 0;   // 0 automatic; kStageFull; kStageRing
   int whole_groups = 0;  // with split > 1: leading n-tile groups kept whole (not split)
   int valu_dot = 0;      // 1: the VALU packed-dot path instead of the MFMA
+  int block_cols = 0;    // one activation row, NVFP4: 0 automatic (on), 1 on, 2 off
 };
 
 constexpr int kStageFull = 1;  // the workgroup's whole K range of x staged before the stream
@@ -29,6 +30,7 @@ struct GemmPlan {
   int waves;
   int k_slices;    // wavefronts of a workgroup that split one n-tile's K range
   int dot_rows;    // 0: MFMA; 1, 2 or 4: the VALU packed-dot path for up to that many rows
+  int block_cols;  // 1: MFMA output columns carry K-blocks (one activation row, NVFP4, full stage)
   int depth;       // units of the weight stream each wavefront keeps in flight
   int epilogue;    // 0 y[M, N]; 1 h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:]; 2 argmax of each row
   int x_stage;     // kStageFull or kStageRing
@@ -70,7 +72,7 @@ hipError_t launch_fp8_absmax(const uint8_t* codes, const float* row_scales, int6
                              hipStream_t stream);
 hipError_t launch_requantize_fp8_nvfp4(const uint8_t* f8, const float* row_scales, int64_t n, int64_t k,
                                        float tensor_scale, uint8_t* codes, uint8_t* scales, hipStream_t stream);
-hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, int grid,
+hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, int grid, int loads,
                                hipStream_t stream);
 int read_ceiling_default_grid();
 

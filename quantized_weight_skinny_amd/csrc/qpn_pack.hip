@@ -300,20 +300,20 @@ __global__ __launch_bounds__(kBlock) void quantize_fp8_kernel(const float* __res
   for (int64_t i = threadIdx.x; i < K; i += kBlock) dst[i] = static_cast<uint8_t>(encode_e4m3(src[i] / s));
 }
 
-// Read-only stream: four 16-byte loads in flight per thread, XOR-folded so
-// the loads stay live; one word per wavefront is written.
+// Read-only stream: U 16-byte loads in flight per thread (grid-stride),
+// XOR-folded so the loads stay live; one word per wavefront is written.
+template <int U>
 __global__ __launch_bounds__(kBlock) void read_ceiling_kernel(const u4* __restrict__ buf,
                                                               int64_t n16, uint32_t* __restrict__ sink) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
   int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   uint32_t acc = 0u;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u4 a = __builtin_nontemporal_load(buf + i);
-    const u4 b = __builtin_nontemporal_load(buf + i + stride);
-    const u4 c = __builtin_nontemporal_load(buf + i + 2 * stride);
-    const u4 d = __builtin_nontemporal_load(buf + i + 3 * stride);
-    const u4 e = a ^ b ^ c ^ d;
-    acc ^= e.x ^ e.y ^ e.z ^ e.w;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u4 v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) v[j] = __builtin_nontemporal_load(buf + i + j * stride);
+#pragma unroll
+    for (int j = 0; j < U; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
   for (; i < n16; i += stride) {
     const u4 a = __builtin_nontemporal_load(buf + i);
@@ -429,10 +429,16 @@ int read_ceiling_default_grid() {
   return cus * 8;
 }
 
-hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, int grid,
+hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, int grid, int loads,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(read_ceiling_kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, stream,
-                     static_cast<const u4*>(buf), static_cast<int64_t>(bytes / 16), sink);
+  const u4* b = static_cast<const u4*>(buf);
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  const dim3 g(static_cast<unsigned>(grid)), t(kBlock);
+  switch (loads) {
+    case 2: hipLaunchKernelGGL(read_ceiling_kernel<2>, g, t, 0, stream, b, n16, sink); break;
+    case 8: hipLaunchKernelGGL(read_ceiling_kernel<8>, g, t, 0, stream, b, n16, sink); break;
+    default: hipLaunchKernelGGL(read_ceiling_kernel<4>, g, t, 0, stream, b, n16, sink); break;
+  }
   return hipGetLastError();
 }
 

@@ -99,10 +99,19 @@ class PackedWeight:
         return self.packed.numel() + extra
 
 
-def _raise_bad(bad, where):
-    count = int(bad.item())
-    if count:
-        raise QpnError(QPN_ERR_BAD_CODE, f"{where}: {count} invalid E4M3 code(s) (NaN, or a sign-set block scale)")
+def _pack(call, bad, where, check):
+    """Run a pack call; the C call itself returns QPN_ERR_BAD_CODE for invalid
+    codes (after it has written every packed byte). check=False keeps the
+    packed bytes anyway (layout round-trip tests of every byte value)."""
+    try:
+        call()
+    except QpnError as e:
+        if e.status != QPN_ERR_BAD_CODE:
+            raise
+        if check:
+            count = int(bad.item())
+            raise QpnError(QPN_ERR_BAD_CODE,
+                           f"{where}: {count} invalid E4M3 code(s) (NaN, or a sign-set block scale)") from None
 
 
 def pack_nvfp4(codes, block_scales, tensor_scale, n, k, check=True):
@@ -113,11 +122,9 @@ def pack_nvfp4(codes, block_scales, tensor_scale, n, k, check=True):
     _count(block_scales, n * (k // 16), "block_scales")
     nbytes = qpn_packed_bytes(QPN_FMT_NVFP4, n, k)
     packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
-    bad = torch.zeros(1, dtype=torch.int32, device=codes.device) if check else None
-    qpn_pack_nvfp4(codes.data_ptr(), block_scales.data_ptr(), n, k, packed.data_ptr(), nbytes,
-                   bad.data_ptr() if check else None, _stream())
-    if check:
-        _raise_bad(bad, "qpn_pack_nvfp4")
+    bad = torch.zeros(1, dtype=torch.int32, device=codes.device)
+    _pack(lambda: qpn_pack_nvfp4(codes.data_ptr(), block_scales.data_ptr(), n, k, packed.data_ptr(), nbytes,
+                                 bad.data_ptr(), _stream()), bad, "qpn_pack_nvfp4", check)
     return PackedWeight(QPN_FMT_NVFP4, n, k, packed[:nbytes] if nbytes else packed, tensor_scale)
 
 
@@ -129,11 +136,9 @@ def pack_fp8(codes, row_scales, n, k, check=True):
     _count(row_scales, n, "row_scales")
     nbytes = qpn_packed_bytes(QPN_FMT_FP8_E4M3, n, k)
     packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=codes.device)
-    bad = torch.zeros(1, dtype=torch.int32, device=codes.device) if check else None
-    qpn_pack_fp8(codes.data_ptr(), n, k, packed.data_ptr(), nbytes, bad.data_ptr() if check else None,
-                 _stream())
-    if check:
-        _raise_bad(bad, "qpn_pack_fp8")
+    bad = torch.zeros(1, dtype=torch.int32, device=codes.device)
+    _pack(lambda: qpn_pack_fp8(codes.data_ptr(), n, k, packed.data_ptr(), nbytes, bad.data_ptr(), _stream()), bad,
+          "qpn_pack_fp8", check)
     return PackedWeight(QPN_FMT_FP8_E4M3, n, k, packed[:nbytes] if nbytes else packed, 1.0, row_scales)
 
 
@@ -208,24 +213,25 @@ def requantize_fp8_to_nvfp4(codes8, row_scales):
 
 
 def _launch(split_k=0, waves=0, depth=0, k_slices=0, epilogue=QPN_EPILOGUE_NONE, x_stage=0, whole_groups=0,
-            valu_dot=0):
-    if split_k or waves or depth or k_slices or epilogue or x_stage or whole_groups or valu_dot:
-        return make_launch(split_k, waves, depth, k_slices, epilogue, x_stage, whole_groups, valu_dot)
+            valu_dot=0, block_columns=0):
+    if split_k or waves or depth or k_slices or epilogue or x_stage or whole_groups or valu_dot or block_columns:
+        return make_launch(split_k, waves, depth, k_slices, epilogue, x_stage, whole_groups, valu_dot, block_columns)
     return None
 
 
 def workspace_bytes(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, x_stage=0, whole_groups=0,
-                    valu_dot=0):
+                    valu_dot=0, block_columns=0):
     launch = _launch(split_k, waves, depth, k_slices, QPN_EPILOGUE_SWIGLU if swiglu else QPN_EPILOGUE_NONE, x_stage,
-                     whole_groups, valu_dot)
+                     whole_groups, valu_dot, block_columns)
     d = pw.desc()
     return qpn_workspace_bytes_tuned(d, m, launch) if launch is not None else qpn_workspace_bytes(d, m)
 
 
 def new_workspace(pw, m, split_k=0, waves=0, depth=0, k_slices=0, swiglu=False, device="cuda", x_stage=0,
-                  whole_groups=0, valu_dot=0):
+                  whole_groups=0, valu_dot=0, block_columns=0):
     """A zeroed workspace for gemm(pw) with m rows (None when none is needed)."""
-    need = workspace_bytes(pw, m, split_k, waves, depth, k_slices, swiglu, x_stage, whole_groups, valu_dot)
+    need = workspace_bytes(pw, m, split_k, waves, depth, k_slices, swiglu, x_stage, whole_groups, valu_dot,
+                           block_columns)
     return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
 
 
@@ -246,15 +252,16 @@ def _run(x, pw, out, workspace, launch, cols, dtype=torch.float16):
 
 
 def gemm(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0, whole_groups=0,
-         valu_dot=0):
+         valu_dot=0, block_columns=0):
     """y[m, n] = x[m, k] @ dequant(W)^T in fp16 through qpn_gemm (any shape
-    field set: qpn_gemm_tuned; valu_dot=1: the VALU packed-dot path).
+    field set: qpn_gemm_tuned; valu_dot=1: the VALU packed-dot path;
+    block_columns=1/2: the block-column MFMA path at m=1 on / off).
 
     A workspace, when one is needed and not given, is allocated zeroed per
     call; pass one from new_workspace() to reuse it across calls."""
     return _run(x, pw, out, workspace,
                 _launch(split_k, waves, depth, k_slices, x_stage=x_stage, whole_groups=whole_groups,
-                        valu_dot=valu_dot), pw.n)
+                        valu_dot=valu_dot, block_columns=block_columns), pw.n)
 
 
 def gemm_f32(x, pw, out=None, workspace=None, split_k=0, waves=0, depth=0, k_slices=0, x_stage=0, whole_groups=0):
@@ -307,10 +314,14 @@ def gemm_argmax(x, pw, idx=None, val=None, workspace=None, split_k=0, waves=0, d
     return idx, val
 
 
-def read_ceiling(buf, grid=0, sink=None):
-    """One pass of the read-only streaming kernel over a uint8 CUDA tensor."""
+def read_ceiling(buf, grid=0, sink=None, loads=0):
+    """One pass of the read-only streaming kernel over a uint8 CUDA tensor
+    (``loads`` 16-byte loads in flight per thread: 2, 4 or 8; 0 = 4)."""
     g = grid or qpn_read_ceiling_grid()
     if sink is None:
         sink = torch.empty(g * 4, dtype=torch.int32, device=buf.device)
-    qpn_read_ceiling(buf.data_ptr(), buf.numel() - buf.numel() % 16, sink.data_ptr(), g, _stream())
+    _count(sink, sink.numel(), "sink")
+    if sink.numel() < g * 4:
+        raise ValueError(f"sink must hold {g * 4} words")
+    qpn_read_ceiling(buf.data_ptr(), buf.numel() - buf.numel() % 16, sink.data_ptr(), g, loads, _stream())
     return sink

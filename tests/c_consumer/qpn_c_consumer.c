@@ -47,6 +47,7 @@ int main(void) {
   printf("offset_weight_row_scales %d\n", (int)offsetof(qpn_weight, row_scales));
   printf("sizeof_launch %d\n", (int)sizeof(qpn_launch));
   printf("offset_launch_whole_groups %d\n", (int)offsetof(qpn_launch, whole_groups));
+  printf("offset_launch_block_columns %d\n", (int)offsetof(qpn_launch, block_columns));
   printf("max_m %d\n", QPN_MAX_M);
 
   if (strcmp(qpn_status_string(QPN_OK), "ok") != 0) FAIL("status string");

@@ -60,6 +60,7 @@ def test_header_compiles_as_c99_and_links(tmp_path):
     assert int(got["offset_weight_row_scales"]) == q.qpn_weight.row_scales.offset
     assert int(got["sizeof_launch"]) == ctypes.sizeof(q.qpn_launch)
     assert int(got["offset_launch_whole_groups"]) == q.qpn_launch.whole_groups.offset
+    assert int(got["offset_launch_block_columns"]) == q.qpn_launch.block_columns.offset
     assert int(got["max_m"]) == q.QPN_MAX_M
     w = _w(n=34816, k=5120)
     p = q.qpn_gemm_plan(w, 1)
@@ -268,6 +269,38 @@ def test_valu_dot_plans_and_checks():
     assert p.x_stage == q.QPN_X_STAGE_FULL and 2 * 4 * (-(-68 // p.split_k) * 256 + 8) <= 79 * 1024
 
 
+def test_block_columns_plans_and_checks():
+    """Block columns: one activation row of NVFP4 weights with a full stage,
+    only on request (1); 0 and 2 leave it off, other values are refused."""
+    unsup, err = q.QPN_ERR_UNSUPPORTED, q.QPN_ERR_INVALID_ARG
+    full, ring = q.QPN_X_STAGE_FULL, q.QPN_X_STAGE_RING
+    w = _w(n=5120, k=17408)
+    assert _plan(w, 1, x_stage=full).block_columns == 2
+    assert _plan(w, 1, x_stage=full, block_columns=2).block_columns == 2
+    assert _plan(w, 1, x_stage=full, block_columns=1).block_columns == 1
+    for m in range(2, 17):
+        assert _plan(w, m).block_columns == 2
+        assert _plan(w, m, block_columns=1) == unsup
+    assert _plan(w, 1, x_stage=ring).block_columns == 2
+    assert _plan(w, 1, x_stage=ring, block_columns=1) == unsup
+    assert _plan(w, 1, valu_dot=1).block_columns == 2
+    assert _plan(w, 1, valu_dot=1, block_columns=1) == unsup
+    w8 = _w(fmt=q.QPN_FMT_FP8_E4M3, n=5120, k=17408)
+    assert _plan(w8, 1, x_stage=full).block_columns == 2
+    assert _plan(w8, 1, x_stage=full, block_columns=1) == unsup
+    for e in (q.QPN_EPILOGUE_F32, q.QPN_EPILOGUE_SWIGLU, q.QPN_EPILOGUE_ARGMAX):
+        assert _plan(w, 1, x_stage=full, epilogue=e).block_columns == 2
+        assert _plan(w, 1, x_stage=full, epilogue=e, block_columns=1).block_columns == 1
+    # the zero region the B operand reads is part of the LDS budget: a full
+    # stage that fills the budget has no room for it
+    assert _plan(_w(n=512, k=157 * 256), 1, x_stage=full, split_k=1).block_columns == 2
+    assert _plan(_w(n=512, k=157 * 256), 1, x_stage=full, split_k=1, block_columns=1) == unsup
+    for bad in (3, -1):
+        assert _plan(w, 1, block_columns=bad) == err
+        launch = q.make_launch(block_columns=bad)
+        assert q.lib().qpn_gemm_tuned(FAKE, ctypes.byref(w), FAKE, 1, None, 0, ctypes.byref(launch), None) == err
+
+
 def test_whole_groups_plans():
     unsup, err = q.QPN_ERR_UNSUPPORTED, q.QPN_ERR_INVALID_ARG
     ring, full = q.QPN_X_STAGE_RING, q.QPN_X_STAGE_FULL
@@ -423,19 +456,26 @@ def test_requantize_rejects_bad_arguments():
 def test_pack_and_quantize_reject_bad_arguments():
     lib = q.lib()
     nv = q.qpn_packed_bytes(q.QPN_FMT_NVFP4, 32, 64)
-    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 64, FAKE, nv - 1, None, None) == q.QPN_ERR_BUFFER_TOO_SMALL
-    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 64, FAKE + 8, nv, None, None) == q.QPN_ERR_INVALID_ARG
-    assert lib.qpn_pack_nvfp4(None, FAKE, 32, 64, FAKE, nv, None, None) == q.QPN_ERR_INVALID_ARG
-    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 40, FAKE, nv, None, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 64, FAKE, nv - 1, FAKE, None) == q.QPN_ERR_BUFFER_TOO_SMALL
+    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 64, FAKE + 8, nv, FAKE, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_pack_nvfp4(None, FAKE, 32, 64, FAKE, nv, FAKE, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 40, FAKE, nv, FAKE, None) == q.QPN_ERR_INVALID_ARG
+    # the invalid-code counter is required (pack reports invalid codes itself)
+    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 64, FAKE, nv, None, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_pack_nvfp4(FAKE, FAKE, 32, 64, FAKE, nv, FAKE + 2, None) == q.QPN_ERR_INVALID_ARG
     assert lib.qpn_pack_nvfp4(None, None, 0, 64, None, 0, None, None) == q.QPN_OK  # empty
     f8 = q.qpn_packed_bytes(q.QPN_FMT_FP8_E4M3, 32, 64)
-    assert lib.qpn_pack_fp8(FAKE, 32, 64, FAKE, f8 - 16, None, None) == q.QPN_ERR_BUFFER_TOO_SMALL
+    assert lib.qpn_pack_fp8(FAKE, 32, 64, FAKE, f8 - 16, FAKE, None) == q.QPN_ERR_BUFFER_TOO_SMALL
+    assert lib.qpn_pack_fp8(FAKE, 32, 64, FAKE, f8, None, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_pack_fp8(FAKE, 32, 64, FAKE, f8, FAKE + 1, None) == q.QPN_ERR_INVALID_ARG
     assert lib.qpn_unpack_fp8(FAKE, f8, -2, 64, FAKE, None) == q.QPN_ERR_INVALID_ARG
     assert lib.qpn_quantize_nvfp4(FAKE, 4, 64, 0.0, FAKE, FAKE, None) == q.QPN_ERR_INVALID_ARG
     assert lib.qpn_quantize_nvfp4(FAKE, 4, 64, float("inf"), FAKE, FAKE, None) == q.QPN_ERR_INVALID_ARG
     assert lib.qpn_quantize_fp8(FAKE, 4, 64, FAKE, None, None) == q.QPN_ERR_INVALID_ARG
     assert lib.qpn_absmax_f32(FAKE, -1, FAKE, None) == q.QPN_ERR_INVALID_ARG
-    assert lib.qpn_read_ceiling(FAKE, 100, FAKE, 0, None) == q.QPN_ERR_INVALID_ARG  # bytes % 16
+    assert lib.qpn_read_ceiling(FAKE, 100, FAKE, 0, 0, None) == q.QPN_ERR_INVALID_ARG  # bytes % 16
+    assert lib.qpn_read_ceiling(FAKE, 96, FAKE, 0, 3, None) == q.QPN_ERR_INVALID_ARG   # loads 2, 4 or 8
+    assert lib.qpn_read_ceiling(FAKE, 96, FAKE, -1, 4, None) == q.QPN_ERR_INVALID_ARG  # grid
 
 
 def test_product_package_does_not_import_the_oracle():

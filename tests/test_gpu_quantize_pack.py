@@ -9,6 +9,7 @@ import oracle
 import workloads
 from golden_io import load_case
 from gpu_helpers import DEV, oracle_quantize, say, to_dev, to_host
+import quantized_weight_skinny_amd as q
 from quantized_weight_skinny_amd import QPN_ERR_BAD_CODE, QpnError
 from quantized_weight_skinny_amd import torch_api as qt
 
@@ -146,6 +147,45 @@ def test_pack_unpack_fp8_round_trip(n, k):
     pw = qt.pack_fp8(to_dev(codes), to_dev(rs), n, k)
     (c2,) = qt.unpack(pw)
     assert np.array_equal(to_host(c2), codes)
+
+
+def _c_pack(fmt, codes, scales, n, k):
+    """The C entry point itself (ctypes, no torch wrapper): (status, count)."""
+    lib = q.lib()
+    nbytes = q.qpn_packed_bytes(q.QPN_FMT_NVFP4 if fmt == "nvfp4" else q.QPN_FMT_FP8_E4M3, n, k)
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    bad = torch.full((1,), 12345, dtype=torch.int32, device=DEV)   # the call clears it
+    c = to_dev(codes)
+    s = torch.cuda.current_stream().cuda_stream
+    if fmt == "nvfp4":
+        st = lib.qpn_pack_nvfp4(c.data_ptr(), to_dev(scales).data_ptr(), n, k, packed.data_ptr(), nbytes,
+                                bad.data_ptr(), s)
+    else:
+        st = lib.qpn_pack_fp8(c.data_ptr(), n, k, packed.data_ptr(), nbytes, bad.data_ptr(), s)
+    return st, int(to_host(bad)[0])
+
+
+def test_c_pack_returns_bad_code():
+    """qpn_pack_* report invalid E4M3 codes through their own status:
+    QPN_ERR_BAD_CODE (-3) for NaN (0x7F, 0xFF) and sign-set block scales and
+    for NaN FP8 weights, QPN_OK otherwise, with the count in the counter."""
+    say("c pack bad code")
+    n, k = 32, 512
+    codes = workloads.random_nibble_bytes(n, k, 3)
+    ok = workloads.random_block_scale_codes(n, k, 4)
+    assert _c_pack("nvfp4", codes, ok, n, k) == (q.QPN_OK, 0)
+    for bad_code in (0x7F, 0xFF, 0x80, 0xB8, 0xFE):
+        sc = ok.copy()
+        sc[5, 3] = bad_code
+        assert _c_pack("nvfp4", codes, sc, n, k) == (q.QPN_ERR_BAD_CODE, 1), hex(bad_code)
+    sc = ok.copy()
+    sc[0, 0], sc[31, 31], sc[7, 2] = 0x7F, 0xFF, 0x80
+    assert _c_pack("nvfp4", codes, sc, n, k) == (q.QPN_ERR_BAD_CODE, 3)
+    f8 = workloads.random_fp8_codes(n, k, 5)
+    f8 = np.where((f8 & 0x7F) == 0x7F, f8 ^ 1, f8).astype(np.uint8)
+    assert _c_pack("fp8", f8, None, n, k) == (q.QPN_OK, 0)
+    f8[1, 1], f8[2, 2] = 0x7F, 0xFF
+    assert _c_pack("fp8", f8, None, n, k) == (q.QPN_ERR_BAD_CODE, 2)
 
 
 def test_pack_counts_invalid_codes():
