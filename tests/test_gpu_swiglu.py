@@ -106,8 +106,9 @@ def test_swiglu_of_zero_gate_and_one_hot_rows():
 
 @pytest.mark.parametrize("m", [1, 8])
 def test_swiglu_full_size_gate_up(m):
-    """The 27B gate_up (34816 x 5120 NVFP4) with the fused epilogue; the
-    oracle recomputes sampled h columns from their gate and up rows."""
+    """The 27B gate_up (34816 x 5120 NVFP4) with the fused epilogue: on
+    quantized weights the oracle recomputes sampled h columns from their gate
+    and up rows; on seeded canonical codes it recomputes every h column."""
     n, k = workloads.SHAPES["gate_up"]
     say("swiglu full size", m)
     wl = "nvfp4_27b_mlp"
@@ -125,5 +126,16 @@ def test_swiglu_full_size_gate_up(m):
     parts = oracle.quantize_nvfp4(w[rows], tensor_scale=s_t)
     y_ref, b = oracle.gemm_nvfp4(x, *parts)
     _check(h[:, cols], y_ref, b, f"gate_up swiglu m={m}")
+    del pw
+    # every h column, on seeded canonical codes (the oracle only dequantizes)
+    codes = workloads.random_nibble_bytes(n, k, 17 + m)
+    scales = workloads.random_block_scale_codes(n, k, 18 + m, lo=0x20, hi=0x40)
+    pw = qt.pack_nvfp4(to_dev(codes), to_dev(scales), 2.0 ** -6, n, k)
+    h = to_host(qt.gemm_swiglu(to_dev(x), pw))
+    for c0 in range(0, half, 8192):
+        cols = np.arange(c0, min(half, c0 + 8192))
+        rows = np.concatenate([cols, cols + half])
+        y_ref, b = oracle.gemm_nvfp4(x, oracle.unpack_nibbles(codes[rows]), scales[rows], np.float32(2.0 ** -6))
+        _check(h[:, cols], y_ref, b, f"gate_up swiglu m={m} columns {c0}..")
     del pw
     torch.cuda.empty_cache()
