@@ -288,6 +288,25 @@ size_t qpn_workspace_bytes_tuned(const qpn_weight* w, int32_t m, const qpn_launc
 qpn_status qpn_gemm_plan(const qpn_weight* w, int32_t m, const qpn_launch* launch, qpn_launch* resolved);
 
 /*
+ * qpn_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same launch and kernels as qpn_gemm with no workspace argument. The split-K
+ * counters and fp32 partial sums go to a scratch array the library holds in
+ * device memory, one per GPU it runs on, of QPN_NOALLOC_SCRATCH_BYTES bytes,
+ * kept until the process ends. The call allocates nothing.
+ *   Arguments and results as in qpn_gemm.
+ *   A shape whose launch needs more scratch than that (qpn_workspace_bytes
+ *   above QPN_NOALLOC_SCRATCH_BYTES) returns QPN_ERR_BUFFER_TOO_SMALL and
+ *   enqueues nothing; QPN_ERR_HIP if the scratch address cannot be taken.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (other streams, other threads) race and must not be issued; calls
+ * in order on one stream are safe, and each leaves the counters at zero for
+ * the next.
+ */
+#define QPN_NOALLOC_SCRATCH_BYTES (16u << 20)
+qpn_status qpn_gemm_noalloc(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m, void* stream);
+
+/*
  * The gate_up GEMM of a gated MLP with SwiGLU fused into its epilogue. The
  * weight is the row concatenation [W_gate; W_up] (w->n = 2 * F, F a multiple
  * of 16); with g = x W_gate^T and u = x W_up^T (fp32 accumulators, scaled),

@@ -95,6 +95,7 @@ SIGNATURES = {
     "qpn_workspace_bytes_tuned": (_SZ, [_W, _I32, _L]),
     "qpn_gemm_plan": (_I32, [_W, _I32, _L, _L]),
     "qpn_gemm": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
+    "qpn_gemm_noalloc": (_I32, [_P, _W, _P, _I32, _P]),
     "qpn_gemm_tuned": (_I32, [_P, _W, _P, _I32, _P, _SZ, _L, _P]),
     "qpn_gemm_swiglu": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
     "qpn_gemm_f32": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
@@ -220,6 +221,13 @@ def qpn_gemm_tuned(x, weight, y, m, workspace, workspace_bytes, launch, stream):
 def qpn_gemm_swiglu(x, weight, h, m, workspace, workspace_bytes, stream):
     return _check(lib().qpn_gemm_swiglu(x, ctypes.byref(weight), h, m, workspace, workspace_bytes, stream),
                   "qpn_gemm_swiglu")
+
+
+QPN_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def qpn_gemm_noalloc(x, weight, y, m, stream):
+    return _check(lib().qpn_gemm_noalloc(x, ctypes.byref(weight), y, m, stream), "qpn_gemm_noalloc")
 
 
 def qpn_gemm_f32(x, weight, y, m, workspace, workspace_bytes, stream):

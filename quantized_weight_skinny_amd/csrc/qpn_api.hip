@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "qpn_device.hpp"
 #include "qpn_internal.hpp"
 
@@ -300,6 +302,55 @@ qpn_status qpn_gemm_argmax(const void* x_dev, const qpn_weight* w, int32_t* idx_
 qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m,
                     void* workspace_dev, size_t workspace_bytes, void* stream) {
   return qpn_gemm_tuned(x_dev, w, y_dev, m, workspace_dev, workspace_bytes, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The no-allocation variant's scratch: one array per GPU the library runs on,
+// holding the split-K arrival counters (zero at load; every call leaves them
+// zero) and the fp32 partial sums. In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is handed on.
+static __device__ __align__(256) unsigned char scratch[QPN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+qpn_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QPN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return QPN_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QPN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qpn_status qpn_gemm_noalloc(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t m, void* stream) {
+  const qpn_status st = check_weight(w);
+  if (st != QPN_OK) return st;
+  if (m < 0 || m > QPN_MAX_M) return QPN_ERR_INVALID_ARG;
+  if (m == 0 || w->n == 0) return QPN_OK;
+  qpn::GemmPlan p;
+  if (!qpn::plan_gemm(w->format, w->n, w->k, m, qpn::LaunchOverride{}, &p)) return QPN_ERR_UNSUPPORTED;
+  if (p.workspace_bytes > QPN_NOALLOC_SCRATCH_BYTES) return QPN_ERR_BUFFER_TOO_SMALL;
+  void* ws = nullptr;
+  if (p.workspace_bytes) {
+    const qpn_status s2 = scratch_for_current_device(&ws);
+    if (s2 != QPN_OK) return s2;
+  }
+  return gemm_call(x_dev, w, y_dev, nullptr, m, ws, p.workspace_bytes ? QPN_NOALLOC_SCRATCH_BYTES : 0,
+                   qpn::LaunchOverride{}, stream);
 }
 
 qpn_status qpn_gemm_swiglu(const void* x_dev, const qpn_weight* w, void* h_dev, int32_t m,

@@ -34,6 +34,7 @@ int main(void) {
       (entry_fn)qpn_gemm_plan,          (entry_fn)qpn_gemm_swiglu,
       (entry_fn)qpn_gemm_f32,           (entry_fn)qpn_gemm_argmax,
       (entry_fn)qpn_read_ceiling,       (entry_fn)qpn_read_ceiling_grid,
+      (entry_fn)qpn_gemm_noalloc,
   };
   size_t i;
   for (i = 0; i < sizeof entries / sizeof entries[0]; ++i)

@@ -486,3 +486,16 @@ def test_product_package_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_noalloc_checks_before_any_device_call():
+    """qpn_gemm_noalloc: argument checks, and a launch needing more than its
+    scratch is refused before any HIP call."""
+    lib = q.lib()
+    w = q.make_weight(q.QPN_FMT_NVFP4, 1024, 1 << 20, FAKE)
+    assert q.qpn_workspace_bytes(w, 16) > q.QPN_NOALLOC_SCRATCH_BYTES
+    assert lib.qpn_gemm_noalloc(FAKE, ctypes.byref(w), FAKE, 16, None) == q.QPN_ERR_BUFFER_TOO_SMALL
+    assert lib.qpn_gemm_noalloc(FAKE, ctypes.byref(w), FAKE, 17, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_gemm_noalloc(FAKE, None, FAKE, 1, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_gemm_noalloc(FAKE, ctypes.byref(_w(fmt=9)), FAKE, 1, None) == q.QPN_ERR_INVALID_ARG
+    assert lib.qpn_gemm_noalloc(None, ctypes.byref(_w()), FAKE, 0, None) == q.QPN_OK  # nothing to do
