@@ -386,7 +386,7 @@ def read_pair_us(a, b, total=4 << 30, reps=5):
     return us
 
 
-KERNEL_SOURCES = ("qpn_device.hpp", "qpn_gemm.hip", "qpn_internal.hpp")
+KERNEL_SOURCES = ("qpn_device.hpp", "qpn_gemm.hip", "qpn_internal.hpp", "qpn_plan.hpp", "qpn_plan.cpp")
 
 
 def kernel_source_hash():

@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qpn_plan.hpp"
+
 namespace qpn {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -34,16 +36,6 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTileN = 16;
-constexpr int kUnitK = 256;
-constexpr int kNvUnitBytes = 2304;
-constexpr int kF8UnitBytes = 4096;
-constexpr int kMaxM = 16;
-
-constexpr int kFmtNvfp4 = 1;
-constexpr int kFmtFp8 = 2;
-
-__host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // s_waitcnt immediate that waits until at most n vector memory operations
 // are outstanding and leaves the other counters alone (gfx9 encoding:

@@ -1,0 +1,236 @@
+// The launch planner of the skinny GEMM (declared in qpn_plan.hpp): plain
+// host C++, shared by the C ABI and the kernel launcher.
+#include "qpn_plan.hpp"
+
+namespace qpn {
+namespace {
+
+// Launch shapes. For the matrices of a ~27B dense decoder (hidden 5120) the
+// launch comes from a table measured on MI355X: a sweep of activation stage x
+// workgroup size x K slices x K split x stream depth, best graph-replayed time
+// per launch at M = 1, 2, 4, 8, 16 (and, for gate_up, groups kept whole x
+// split of the rest). Other shapes use a rule distilled from the same sweep:
+//  * a workgroup holds TN n-tiles that share one staged copy of x (the
+//    staging reads 2*M bytes of x per K element against 9*TN bytes of NVFP4
+//    weights), TN = 2 up to M = 4 and 4 above;
+//  * the rest of an 8-wavefront workgroup splits each n-tile's K range into
+//    K slices, reduced through LDS, keeping >= kMinSliceUnits units a slice;
+//  * K is split over workgroups only as far as the activation stage must be
+//    cut to fit LDS (that reduction costs memory round trips at the tail);
+//  * a stream depth of 3 units;
+//  * the ring activation stage from kRingMinM rows on (at 8 and 16 rows it
+//    wins on every matrix but one, at 4 it ties with the full stage);
+//  * no whole groups (all groups split alike): a balanced grid needs the
+//    shape's group count, and is only tabled where it was measured.
+struct TunedLaunch {
+  int fmt;
+  int64_t n, k;
+  int m_max;  // entry applies to m <= m_max (entries of a shape in increasing m_max)
+  int waves, k_slices, split, depth;
+  int x_stage = kStageFull;
+  int whole_groups = 0;
+};
+
+constexpr TunedLaunch kTuned[] = {
+    // NVFP4 gate_up 34816 x 5120: 2176 n-tiles. Whole groups of 8 (or 4)
+    // tiles fill the 256 CUs evenly (256 or 512 groups); the last 16 (32)
+    // groups split K four ways, a short tail of small workgroups. At M = 2
+    // the full stage beats the ring (18.5 against 19.4 us, alternated runs).
+    {kFmtNvfp4, 34816, 5120, 1, 8, 1, 4, 2, kStageRing, 256},
+    {kFmtNvfp4, 34816, 5120, 2, 4, 1, 4, 2, kStageFull, 512},
+    {kFmtNvfp4, 34816, 5120, 4, 8, 1, 4, 2, kStageRing, 256},
+    {kFmtNvfp4, 34816, 5120, 16, 4, 1, 4, 2, kStageRing, 512},
+    // NVFP4 down 5120 x 17408
+    {kFmtNvfp4, 5120, 17408, 2, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 17408, 4, 8, 2, 3, 2},
+    {kFmtNvfp4, 5120, 17408, 8, 8, 2, 3, 2, kStageRing}, {kFmtNvfp4, 5120, 17408, 16, 8, 2, 3, 2, kStageRing},
+    // NVFP4 qkv 7168 x 5120 and o_proj 5120 x 5120
+    {kFmtNvfp4, 7168, 5120, 4, 8, 4, 1, 3}, {kFmtNvfp4, 7168, 5120, 8, 8, 4, 1, 2, kStageRing},
+    {kFmtNvfp4, 7168, 5120, 16, 8, 2, 2, 2, kStageRing},
+    {kFmtNvfp4, 5120, 5120, 4, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 5120, 8, 8, 4, 1, 2, kStageRing},
+    {kFmtNvfp4, 5120, 5120, 16, 8, 2, 3, 2},
+    // NVFP4 lm_head 151936 x 5120
+    {kFmtNvfp4, 151936, 5120, 1, 8, 4, 1, 3}, {kFmtNvfp4, 151936, 5120, 2, 4, 2, 1, 2, kStageRing},
+    {kFmtNvfp4, 151936, 5120, 4, 8, 2, 1, 2}, {kFmtNvfp4, 151936, 5120, 16, 8, 1, 1, 2, kStageRing},
+    // Per-GPU shapes of 4-way tensor parallelism (NVFP4): qkv 1792 x 5120,
+    // o_proj 5120 x 1280, gate_up 8704 x 5120, down 5120 x 4352
+    {kFmtNvfp4, 1792, 5120, 1, 4, 4, 1, 3}, {kFmtNvfp4, 1792, 5120, 8, 8, 2, 6, 2},
+    {kFmtNvfp4, 5120, 1280, 8, 8, 4, 1, 2},
+    {kFmtNvfp4, 8704, 5120, 1, 8, 2, 1, 3}, {kFmtNvfp4, 8704, 5120, 8, 4, 2, 6, 2, kStageRing, 256},
+    {kFmtNvfp4, 5120, 4352, 1, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 4352, 8, 8, 4, 1, 2},
+    // FP8 qkv 7168 x 5120
+    {kFmtFp8, 7168, 5120, 2, 4, 2, 1, 2}, {kFmtFp8, 7168, 5120, 4, 4, 2, 1, 3, kStageRing},
+    {kFmtFp8, 7168, 5120, 8, 4, 2, 1, 2, kStageRing}, {kFmtFp8, 7168, 5120, 16, 8, 2, 2, 2, kStageRing},
+    // FP8 o_proj 5120 x 5120
+    {kFmtFp8, 5120, 5120, 1, 4, 2, 1, 3}, {kFmtFp8, 5120, 5120, 2, 4, 2, 1, 4},
+    {kFmtFp8, 5120, 5120, 8, 4, 2, 1, 3, kStageRing}, {kFmtFp8, 5120, 5120, 16, 8, 2, 3, 2, kStageRing},
+    // FP8 down 5120 x 17408
+    {kFmtFp8, 5120, 17408, 1, 8, 4, 1, 2}, {kFmtFp8, 5120, 17408, 4, 4, 1, 3, 3, kStageRing},
+    {kFmtFp8, 5120, 17408, 16, 8, 2, 3, 3, kStageRing},
+};
+
+const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
+  for (const TunedLaunch& t : kTuned)
+    if (t.fmt == fmt && t.n == n && t.k == k && m <= t.m_max) return &t;
+  return nullptr;
+}
+
+}  // namespace
+
+int ring_pieces(int waves, int k_slices, int m) { return (k_slices * m * 32 + waves * 64 - 1) / (waves * 64); }
+
+bool shape_ok(int64_t n, int64_t k) {
+  return n >= 0 && k >= 0 && k % 16 == 0 && n <= (int64_t(1) << 31) - 16 && k <= (int64_t(1) << 30);
+}
+
+size_t packed_bytes(int fmt, int64_t n, int64_t k) {
+  if (!shape_ok(n, k)) return 0;
+  const int64_t units = ceil_div(n, kTileN) * ceil_div(k, kUnitK);
+  if (fmt == kFmtNvfp4) return static_cast<size_t>(units) * kNvUnitBytes;
+  if (fmt == kFmtFp8) return static_cast<size_t>(units) * kF8UnitBytes;
+  return 0;
+}
+
+bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, GemmPlan* p) {
+  if (fmt != kFmtNvfp4 && fmt != kFmtFp8) return false;
+  if (m < 1 || m > kMaxM || n < 1 || k < 0) return false;
+  if (!shape_ok(n, k)) return false;
+  // the override's own ranges (0 is automatic for every field)
+  if (o.split < 0 || o.waves < 0 || o.depth < 0 || o.k_slices < 0 || o.whole_groups < 0) return false;
+  if (o.x_stage != 0 && o.x_stage != kStageFull && o.x_stage != kStageRing) return false;
+  if (o.epilogue < kEpiNone || o.epilogue > kEpiF32) return false;
+  if (o.valu_dot != 0 && o.valu_dot != 1) return false;
+  if (o.block_cols < 0 || o.block_cols > 2) return false;
+  const int64_t NT = ceil_div(n, kTileN);
+  const int64_t KU = ceil_div(k, kUnitK);
+  const int64_t unit_bytes = fmt == kFmtNvfp4 ? kNvUnitBytes : kF8UnitBytes;
+  // unit offsets inside one wavefront's stream are 32-bit
+  if (NT * KU * unit_bytes >= (int64_t(1) << 31)) return false;
+  const int64_t max_ups = (static_cast<int64_t>(kLdsBudget) / (2 * m) - kRowPad) / kUnitK;
+  if (max_ups < 1) return false;
+
+  // A tuned launch for this shape fills in what the caller left automatic
+  // (the argmax epilogue takes the plain GEMM's shape: on the 151936-row
+  // head it measured the same as few, wide groups, 70.2 against 70.4 us at
+  // M = 1 and 70.1 against 70.2 at M = 8).
+  LaunchOverride w = o;
+  if (const TunedLaunch* t = find_tuned(fmt, n, k, m)) {
+    if (!w.split) w.split = t->split;
+    if (!w.waves) w.waves = t->waves;
+    if (!w.k_slices) w.k_slices = t->k_slices;
+    if (!w.depth) w.depth = t->depth;
+    if (!w.x_stage) w.x_stage = t->x_stage;
+    if (!w.whole_groups && !o.split) w.whole_groups = t->whole_groups;
+  }
+
+  // K ranges over workgroups: as few as a full activation stage allows.
+  int64_t split = w.split > 0 ? w.split : (KU ? ceil_div(KU, max_ups) : 1);
+  if (split > KU) split = KU ? KU : 1;
+  if (split < 1) split = 1;
+  const int64_t ups = KU ? ceil_div(KU, split) : 0;
+  if (KU) split = ceil_div(KU, ups);
+
+  // n-tiles per workgroup first (from M), then as many K slices per n-tile
+  // as the workgroup has room for and the K range supports.
+  const int tn_target = m > 4 ? 4 : 2;
+  int ks = w.k_slices;
+  if (!ks) {
+    const int ks_room = 8 / tn_target;
+    ks = 1;
+    while (ks < ks_room && ceil_div(ups, 2 * ks) >= kMinSliceUnits) ks *= 2;
+  }
+  int waves = w.waves;
+  if (!waves) {
+    waves = tn_target * ks < 4 ? 4 : tn_target * ks > 8 ? 8 : tn_target * ks;
+    if (waves < ks) waves = ks;
+  }
+  // The SwiGLU epilogue pairs gate and up n-tiles inside a workgroup, so it
+  // needs an even number of n-tiles per workgroup (and N/2 on a tile
+  // boundary): an automatic shape gives up K slices (or adds wavefronts) to
+  // get there.
+  if (o.epilogue == kEpiSwiglu) {
+    if (n % (2 * kTileN)) return false;
+    if (waves && ks && (waves / ks) % 2) {
+      if (o.k_slices && o.waves) return false;
+      if (!o.k_slices && ks > 1) ks /= 2;
+      else if (!o.waves && waves < 8) waves *= 2;
+      else return false;
+    }
+  }
+  if (waves != 4 && waves != 8) return false;
+  if (ks != 1 && ks != 2 && ks != 4 && ks != 8) return false;
+  if (ks > waves) return false;
+  if (o.epilogue == kEpiSwiglu && (waves / ks) % 2) return false;
+  const int depth = w.depth ? w.depth : 3;
+  if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
+  // The packed-dot path: the plain epilogue, a full stage, depths 2..4, and
+  // at most 4 rows (its cost grows with M; the MFMA's does not).
+  if (o.valu_dot && (o.epilogue != kEpiNone || depth > 4 || m > 4 || o.x_stage == kStageRing)) return false;
+
+  // Groups kept whole (split > 1 only): a whole group's workgroup covers
+  // all KU units, so a full stage must hold them.
+  const int64_t groups = ceil_div(NT, waves / ks);
+  const int64_t whole = split > 1 ? (w.whole_groups < groups ? w.whole_groups : groups) : groups;
+  if (w.whole_groups < 0) return false;
+
+  // Activation stage: the caller's choice is binding; a tuned or automatic
+  // one falls back to the other stage when it is not possible. The ring
+  // stage wins from kRingMinM rows on (its per-unit barriers cost more than
+  // a small full stage saves).
+  const bool full_ok = (split > 1 && whole > 0 ? KU : ups) <= max_ups;
+  const bool ring_ok = depth <= 4 && ring_pieces(waves, ks, m) <= kRingMaxPieces &&
+                       2 * static_cast<int64_t>(m) * k < (int64_t(1) << 31);
+  int stage = o.valu_dot ? kStageFull : w.x_stage ? w.x_stage : (m >= kRingMinM ? kStageRing : kStageFull);
+  if (stage != kStageFull && stage != kStageRing) return false;
+  if (!o.x_stage && !o.valu_dot) {
+    if (stage == kStageRing && !ring_ok) stage = kStageFull;
+    if (stage == kStageFull && !full_ok) stage = kStageRing;
+  }
+  if (stage == kStageFull ? !full_ok : !ring_ok) return false;
+  // Block columns: one activation row of NVFP4 weights, full stage, the MFMA
+  // path; 1 demands it, 0 and 2 leave it off. Its decode skips the
+  // per-weight scale multiply (45 instead of 66 VALU per unit), yet measured
+  // 2-5% slower as a standalone launch (11.2 against 11.0 us on down at one
+  // row, 18.2 against 17.9 on gate_up): the launch is bound by memory latency
+  // and balance, not by the VALU, and the path adds four LDS permutes a unit.
+  if (o.block_cols < 0 || o.block_cols > 2) return false;
+  const int64_t staged = (split > 1 && whole > 0 ? KU : ups) * kUnitK + kRowPad;  // halves per staged row
+  const bool bc_ok = m == 1 && fmt == kFmtNvfp4 && stage == kStageFull && !o.valu_dot &&
+                     (staged + depth * kUnitK + 64) * static_cast<int64_t>(kHalfBytes) <=
+                         static_cast<int64_t>(kLdsBudget);
+  if (o.block_cols == 1 && !bc_ok) return false;
+  p->block_cols = bc_ok && o.block_cols == 1 ? 1 : 0;
+
+  p->split = static_cast<int>(split);
+  p->whole_groups = split > 1 ? static_cast<int>(whole) : 0;
+  p->waves = waves;
+  p->depth = depth;
+  p->k_slices = ks;
+  p->dot_rows = o.valu_dot ? (m <= 1 ? 1 : m <= 2 ? 2 : 4) : 0;
+  p->units_per_split = static_cast<int>(ups);
+  p->lds_stride = static_cast<int>((split > 1 && whole > 0 ? KU : ups) * kUnitK + kRowPad);
+  p->x_stage = stage;
+  p->lds_bytes = stage == kStageFull ? static_cast<size_t>(m) * p->lds_stride * kHalfBytes
+                                     : static_cast<size_t>(ks) * kRingSlots * m * kRingRow * kHalfBytes;
+  // ... plus the zero region the block-column B operand reads (DEPTH units and a chunk of slack)
+  if (p->block_cols) p->lds_bytes += static_cast<size_t>(depth * kUnitK + 64) * kHalfBytes;
+  // K slices reduce through the same LDS: one 16x16 fp32 tile per wavefront.
+  const size_t red_bytes = ks > 1 ? static_cast<size_t>(waves) * 64 * kTileLaneBytes : 0;
+  if (p->lds_bytes < red_bytes) p->lds_bytes = red_bytes;
+  // ... and (SwiGLU) the up tiles handed to the gate wavefronts.
+  const size_t xch_bytes = o.epilogue == kEpiSwiglu ? static_cast<size_t>(waves / ks / 2) * 64 * kTileLaneBytes : 0;
+  if (p->lds_bytes < xch_bytes) p->lds_bytes = xch_bytes;
+  if (o.epilogue < kEpiNone || o.epilogue > kEpiF32) return false;
+  p->epilogue = o.epilogue;
+  const size_t counters = (static_cast<size_t>(NT) * sizeof(int) + 255) & ~size_t(255);
+  p->control_offset = counters;
+  p->partials_offset = counters + kControlBytes;
+  p->workspace_bytes = 0;
+  if (split > 1)
+    p->workspace_bytes =
+        p->partials_offset + ((static_cast<size_t>(split) * m * n * sizeof(float) + 255) & ~size_t(255));
+  if (o.epilogue == kEpiArgmax && p->workspace_bytes < p->partials_offset)
+    p->workspace_bytes = p->partials_offset;  // the key slots of the control block
+  return true;
+}
+
+}  // namespace qpn
