@@ -366,6 +366,55 @@ qpn_status qpn_gemm_argmax(const void* x_dev, const qpn_weight* w, int32_t* idx_
                            void* workspace_dev, size_t workspace_bytes, const qpn_launch* launch, void* stream);
 
 /*
+ * The MLP of a decoder layer: h = SwiGLU(x W_gate^T, x W_up^T) as in
+ * qpn_gemm_swiglu, then y = h W_down^T as in qpn_gemm, in ONE launch where
+ * possible ([P3] "What I actually built": the dense layer's gate_up and down
+ * projections, streamed back to back). In that launch the down workgroups
+ * start streaming their weights while the last gate_up workgroups still run
+ * and read h as soon as all of it is written, so the chip does not idle
+ * between the two GEMMs.
+ *   gate_up   [W_gate; W_up], n = 2 * F (F a multiple of 16), k = K.
+ *   down      n = N, k = F.
+ *   x_dev     fp16 [m][K], 16-byte aligned.
+ *   h_dev     fp16 [m][F] output (the SwiGLU values, as qpn_gemm_swiglu
+ *             writes them), 16-byte aligned.
+ *   y_dev     fp16 [m][N] output (as qpn_gemm on h), 2-byte aligned.
+ *   launch    NULL (automatic) or a launch shape; `launches` (host, may be
+ *             NULL) gets the number of kernels enqueued, 1 or 2.
+ * The one-launch form needs NVFP4 weights and a grid that fits on the
+ * device at once (the call checks the occupancy; the down workgroups stage
+ * their K range of h whole, so more rows cut down's K into more ranges and
+ * enlarge the grid); otherwise the call enqueues the two GEMMs (or, with
+ * launch->fused = 1, returns QPN_ERR_UNSUPPORTED). Both forms are within the
+ * GEMMs' bounds; where their launch shapes agree (the 27B shapes at m = 1)
+ * they give the same bits. The workspace is
+ * qpn_mlp_workspace_bytes(gate_up, down, m, launch), 16-byte aligned: the two
+ * GEMMs' workspaces, a 128-byte flag line per down workgroup of the
+ * one-launch form, and a 256-byte control block at its end (an arrival
+ * counter, then at byte 8 a status word the kernel sets to 1, and never
+ * clears, if a wait ran past its bound, in which case that call's results
+ * are undefined). All of it must be zero before the first call; every call
+ * leaves the rest zero. Calls that share a workspace must not run at the
+ * same time, and a one-launch call should not share the device with other
+ * work that could hold the CUs its gate_up workgroups need (the bounded
+ * waits then end the call with the status word set).
+ */
+typedef struct {
+  int32_t fused;        /* 0 automatic (one launch at m = 1), 1 one launch or QPN_ERR_UNSUPPORTED,
+                           2 two launches */
+  int32_t down_depth;   /* one launch: weight units in flight per down wavefront: 0 auto, 2, 3, 4, 6, 8 */
+  int32_t stream_after; /* one launch: gate_up workgroups finished before the down workgroups issue
+                           their first weight units: 0 auto (half of them), -1 at once, else the count */
+  int32_t reserved;     /* 0 */
+} qpn_mlp_launch;
+
+size_t qpn_mlp_workspace_bytes(const qpn_weight* gate_up, const qpn_weight* down, int32_t m,
+                               const qpn_mlp_launch* launch);
+qpn_status qpn_mlp(const void* x_dev, const qpn_weight* gate_up, const qpn_weight* down, void* h_dev, void* y_dev,
+                   int32_t m, void* workspace_dev, size_t workspace_bytes, const qpn_mlp_launch* launch,
+                   int32_t* launches, void* stream);
+
+/*
  * Read-only streaming kernel that measures the HBM read ceiling the GEMM is
  * compared against ([P3] "What I actually built": bandwidth is quoted against
  * a measured read-only ceiling). Reads `bytes` (a multiple of 16) from buf_dev

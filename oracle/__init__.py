@@ -62,7 +62,7 @@ from .gemm import (
     tolerance,
     argmax_candidates,
 )
-from .mlp import silu, split_gate_up, swiglu, swiglu_tolerance
+from .mlp import down_tolerance, gated_mlp, silu, split_gate_up, swiglu, swiglu_tolerance
 from .requantize import dequantize_fp8_f32, requantize_fp8_to_nvfp4
 
 __all__ = [
@@ -70,6 +70,6 @@ __all__ = [
     "decode_e4m3", "encode_e2m1", "encode_e4m3", "quantize_nvfp4",
     "quantize_fp8", "nvfp4_tensor_scale", "pack_nibbles", "unpack_nibbles",
     "dequantize_nvfp4", "dequantize_fp8", "skinny_gemm", "gemm_nvfp4",
-    "gemm_fp8", "tolerance", "argmax_candidates", "silu", "split_gate_up", "swiglu", "swiglu_tolerance",
+    "gemm_fp8", "tolerance", "argmax_candidates", "silu", "split_gate_up", "swiglu", "swiglu_tolerance", "down_tolerance", "gated_mlp",
     "dequantize_fp8_f32", "requantize_fp8_to_nvfp4",
 ]

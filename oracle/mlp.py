@@ -60,3 +60,40 @@ def swiglu_tolerance(y, b):
     lin = sg * tu + np.abs(u) * SILU_SLOPE_MAX * tg + SILU_SLOPE_MAX * tg * tu
     hmax = sg * np.abs(u) + lin
     return lin + (2.0 ** -11 + 1e-6) * hmax + 2.0 ** -24
+
+
+def down_tolerance(h, h_tol, w_down):
+    """Per-element bound on |y_gpu - y| for the down GEMM y = h W_down^T
+    (y[M, N], h[M, F], w_down the dequantized float64 W_down[N, F]) when the
+    GPU's h differs from the exact h by at most h_tol elementwise.
+
+    The down GEMM runs on the GPU's own h, h' = h + e with |e| <= h_tol, and
+    comes within the GEMM bound of its exact result on that input:
+        |y_gpu - h' W^T| <= 2e-3 * sum_k |w[n,k] h'[k]| + 1e-3,
+    while |h' W^T - h W^T| = |sum_k w[n,k] e[k]| <= sum_k |w[n,k]| h_tol[k].
+    With |h'| <= |h| + h_tol:
+        |y_gpu - y| <= |W| h_tol + 2e-3 * |W| (|h| + h_tol) + 1e-3
+    (matrix products over k, written on the transposed layout).
+    """
+    h = np.asarray(h, dtype=np.float64)
+    h_tol = np.asarray(h_tol, dtype=np.float64)
+    aw = np.abs(np.asarray(w_down, dtype=np.float64))
+    return h_tol @ aw.T + 2e-3 * ((np.abs(h) + h_tol) @ aw.T) + 1e-3
+
+
+def gated_mlp(x, w_gate_up, w_down):
+    """(h, h_tol, y, y_tol) of the gated MLP on activations x[M, K]:
+    g | u = x W_gate_up^T exactly (float64), h = silu(g) * u, y = h W_down^T,
+    with the acceptance bounds of a GPU that computes the two GEMMs within
+    2e-3 * sum|w x| + 1e-3 and rounds h once to fp16 (swiglu_tolerance and
+    down_tolerance). w_gate_up [2F, K] and w_down [N, F] are the dequantized
+    float64 weights."""
+    x = np.asarray(x, dtype=np.float64)
+    wg = np.asarray(w_gate_up, dtype=np.float64)
+    y_gu = x @ wg.T
+    b_gu = np.abs(x) @ np.abs(wg).T
+    h = swiglu(y_gu)
+    h_tol = swiglu_tolerance(y_gu, b_gu)
+    wd = np.asarray(w_down, dtype=np.float64)
+    return h, h_tol, h @ wd.T, down_tolerance(h, h_tol, wd)
+

@@ -57,6 +57,15 @@ class qpn_launch(ctypes.Structure):
     ]
 
 
+class qpn_mlp_launch(ctypes.Structure):
+    _fields_ = [
+        ("fused", ctypes.c_int32),
+        ("down_depth", ctypes.c_int32),
+        ("stream_after", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 class qpn_weight(ctypes.Structure):
     _fields_ = [
         ("format", ctypes.c_int32),
@@ -76,6 +85,7 @@ _SZ = ctypes.c_size_t
 _F = ctypes.c_float
 _W = ctypes.POINTER(qpn_weight)
 _L = ctypes.POINTER(qpn_launch)
+_ML = ctypes.POINTER(qpn_mlp_launch)
 
 # name -> (restype, argtypes); the declarations of include/qpn.h
 SIGNATURES = {
@@ -100,6 +110,8 @@ SIGNATURES = {
     "qpn_gemm_swiglu": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
     "qpn_gemm_f32": (_I32, [_P, _W, _P, _I32, _P, _SZ, _P]),
     "qpn_gemm_argmax": (_I32, [_P, _W, _P, _P, _I32, _P, _SZ, _L, _P]),
+    "qpn_mlp_workspace_bytes": (_SZ, [_W, _W, _I32, _ML]),
+    "qpn_mlp": (_I32, [_P, _W, _W, _P, _P, _I32, _P, _SZ, _ML, ctypes.POINTER(_I32), _P]),
     "qpn_read_ceiling": (_I32, [_P, _SZ, _P, _I32, _I32, _P]),
     "qpn_read_ceiling_grid": (_I32, []),
 }
@@ -239,6 +251,23 @@ def qpn_gemm_argmax(x, weight, idx, val, m, workspace, workspace_bytes, launch, 
     return _check(lib().qpn_gemm_argmax(x, ctypes.byref(weight), idx, val, m, workspace, workspace_bytes,
                                         ctypes.byref(launch) if launch is not None else None, stream),
                   "qpn_gemm_argmax")
+
+
+def make_mlp_launch(fused=0, down_depth=0, stream_after=0):
+    return qpn_mlp_launch(fused, down_depth, stream_after, 0)
+
+
+def qpn_mlp_workspace_bytes(gate_up, down, m, launch=None):
+    return lib().qpn_mlp_workspace_bytes(ctypes.byref(gate_up), ctypes.byref(down), m,
+                                         ctypes.byref(launch) if launch is not None else None)
+
+
+def qpn_mlp(x, gate_up, down, h, y, m, workspace, workspace_bytes, launch, stream):
+    """Returns the number of kernels the call enqueued (1 or 2)."""
+    n = ctypes.c_int32(0)
+    _check(lib().qpn_mlp(x, ctypes.byref(gate_up), ctypes.byref(down), h, y, m, workspace, workspace_bytes,
+                         ctypes.byref(launch) if launch is not None else None, ctypes.byref(n), stream), "qpn_mlp")
+    return n.value
 
 
 def qpn_read_ceiling(buf, nbytes, sink, grid, loads, stream):

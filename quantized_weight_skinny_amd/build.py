@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["qpn_api.hip", "qpn_gemm.hip", "qpn_pack.hip", "qpn_plan.cpp", "qpn_checks.cpp"]
+SOURCES = ["qpn_api.hip", "qpn_gemm.hip", "qpn_mlp.hip", "qpn_pack.hip", "qpn_plan.cpp", "qpn_checks.cpp"]
 LIB = os.path.join(HERE, "libqpn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -194,6 +194,27 @@ qpn_status qpn_gemm_noalloc(const void* x_dev, const qpn_weight* w, void* y_dev,
                    qpn::LaunchOverride{}, stream);
 }
 
+qpn_status qpn_mlp(const void* x_dev, const qpn_weight* gate_up, const qpn_weight* down, void* h_dev, void* y_dev,
+                   int32_t m, void* workspace_dev, size_t workspace_bytes, const qpn_mlp_launch* launch,
+                   int32_t* launches, void* stream) {
+  qpn::MlpOverride o;
+  if (!qpn::to_mlp_override(launch, &o)) return QPN_ERR_INVALID_ARG;
+  qpn::MlpPlan p;
+  bool run = false;
+  const qpn_status st =
+      qpn::check_mlp(x_dev, gate_up, down, h_dev, y_dev, m, workspace_dev, workspace_bytes, o, &p, &run);
+  if (launches) *launches = 0;
+  if (st != QPN_OK || !run) return st;
+  const qpn::WeightRef up{gate_up->format, gate_up->packed, gate_up->row_scales, gate_up->tensor_scale, gate_up->n,
+                          gate_up->k};
+  const qpn::WeightRef dn{down->format, down->packed, down->row_scales, down->tensor_scale, down->n, down->k};
+  int n = 0;
+  const hipError_t e = qpn::launch_mlp(p, up, dn, x_dev, h_dev, y_dev, workspace_dev, m, as_stream(stream), &n);
+  if (launches) *launches = n;
+  if (e == hipErrorCooperativeLaunchTooLarge) return QPN_ERR_UNSUPPORTED;
+  return from_hip(e);
+}
+
 qpn_status qpn_gemm_swiglu(const void* x_dev, const qpn_weight* w, void* h_dev, int32_t m,
                            void* workspace_dev, size_t workspace_bytes, void* stream) {
   qpn_launch l{};

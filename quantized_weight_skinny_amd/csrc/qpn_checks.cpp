@@ -178,9 +178,61 @@ qpn_status check_gemm(const void* x, const qpn_weight* w, const void* y, const f
   return QPN_OK;
 }
 
+bool to_mlp_override(const qpn_mlp_launch* l, MlpOverride* o) {
+  *o = MlpOverride{};
+  if (!l) return true;
+  if (l->reserved != 0 || l->fused < 0 || l->fused > 2 || l->stream_after < -1) return false;
+  if (l->down_depth != 0 && l->down_depth != 2 && l->down_depth != 3 && l->down_depth != 4 && l->down_depth != 6 &&
+      l->down_depth != 8)
+    return false;
+  o->fused = l->fused;
+  o->down_depth = l->down_depth;
+  o->stream_after = l->stream_after;
+  return true;
+}
+
+qpn_status check_mlp(const void* x, const qpn_weight* up, const qpn_weight* down, const void* h, const void* y,
+                     int32_t m, const void* workspace, size_t workspace_bytes, const MlpOverride& o, MlpPlan* plan,
+                     bool* run) {
+  *run = false;
+  qpn_status st = check_weight(up);
+  if (st != QPN_OK) return st;
+  st = check_weight(down);
+  if (st != QPN_OK) return st;
+  if (m < 0 || m > QPN_MAX_M) return QPN_ERR_INVALID_ARG;
+  if (up->n % 32 || down->k != up->n / 2) return QPN_ERR_INVALID_ARG;
+  if (m == 0 || up->n == 0 || down->n == 0) return QPN_OK;
+  if (!h || !aligned(h, 16) || !y || !aligned(y, 2)) return QPN_ERR_INVALID_ARG;
+  if (up->k > 0 && (!x || !aligned(x, 16))) return QPN_ERR_INVALID_ARG;
+  const qpn_weight* const both[2] = {up, down};
+  for (const qpn_weight* w : both) {
+    if (w->k > 0 && (!w->packed || !aligned(w->packed, 16))) return QPN_ERR_INVALID_ARG;
+    if (w->format == QPN_FMT_NVFP4 && !isfinite(w->tensor_scale)) return QPN_ERR_INVALID_ARG;
+    if (w->format == QPN_FMT_FP8_E4M3 && (!w->row_scales || !aligned(w->row_scales, 4))) return QPN_ERR_INVALID_ARG;
+  }
+  if (!plan_mlp(up->format, up->n, up->k, down->format, down->n, down->k, m, o, plan)) return QPN_ERR_UNSUPPORTED;
+  if (!workspace || !aligned(workspace, 16)) return QPN_ERR_INVALID_ARG;
+  if (workspace_bytes < plan->workspace_bytes) return QPN_ERR_BUFFER_TOO_SMALL;
+  *run = true;
+  return QPN_OK;
+}
+
 }  // namespace qpn
 
 extern "C" {
+
+size_t qpn_mlp_workspace_bytes(const qpn_weight* gate_up, const qpn_weight* down, int32_t m,
+                               const qpn_mlp_launch* launch) {
+  if (qpn::check_weight(gate_up) != QPN_OK || qpn::check_weight(down) != QPN_OK || m < 1 || m > QPN_MAX_M)
+    return 0;
+  if (gate_up->n % 32 || down->k != gate_up->n / 2 || gate_up->n == 0 || down->n == 0) return 0;
+  qpn::MlpOverride o;
+  if (!qpn::to_mlp_override(launch, &o)) return 0;
+  qpn::MlpPlan p;
+  if (!qpn::plan_mlp(gate_up->format, gate_up->n, gate_up->k, down->format, down->n, down->k, m, o, &p)) return 0;
+  return p.workspace_bytes;
+}
+
 
 const char* qpn_status_string(qpn_status s) {
   switch (s) {

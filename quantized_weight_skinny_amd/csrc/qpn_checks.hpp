@@ -53,4 +53,10 @@ qpn_status check_gemm(const void* x, const qpn_weight* w, const void* y, const f
                       const void* workspace, size_t workspace_bytes, const LaunchOverride& o, GemmPlan* plan,
                       bool* run);
 
+// The fused MLP call: plan (*plan) and checks as for qpn_mlp.
+bool to_mlp_override(const qpn_mlp_launch* l, MlpOverride* o);
+qpn_status check_mlp(const void* x, const qpn_weight* up, const qpn_weight* down, const void* h, const void* y,
+                     int32_t m, const void* workspace, size_t workspace_bytes, const MlpOverride& o, MlpPlan* plan,
+                     bool* run);
+
 }  // namespace qpn

@@ -16,6 +16,23 @@ hipError_t launch_gemm(int fmt, const GemmPlan& plan, const void* x, const void*
                        const float* row_scales, float tensor_scale, void* y, float* val, void* workspace,
                        int m, int64_t n, int64_t k, hipStream_t stream);
 
+// A weight as the launchers take it.
+struct WeightRef {
+  int fmt;
+  const void* packed;
+  const float* row_scales;
+  float tensor_scale;
+  int64_t n, k;
+};
+
+// The MLP of plan p: h = SwiGLU(x W_up^T) (fp16 [m][up.n / 2]) and
+// y = h W_dn^T (fp16 [m][dn.n]); one launch when the plan allows it and its
+// grid fits on the device at once, else the two GEMMs (unless p asks for one
+// launch: then hipErrorCooperativeLaunchTooLarge, nothing enqueued).
+// *launches (may be null) gets the number of launches enqueued.
+hipError_t launch_mlp(const MlpPlan& p, const WeightRef& up, const WeightRef& dn, const void* x, void* h, void* y,
+                      void* workspace, int m, hipStream_t stream, int* launches);
+
 hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                              void* packed, int32_t* bad, hipStream_t stream);
 hipError_t launch_pack_fp8(const uint8_t* codes, int64_t n, int64_t k, void* packed,

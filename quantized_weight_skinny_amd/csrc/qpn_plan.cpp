@@ -233,4 +233,64 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   return true;
 }
 
+int64_t gemm_grid(const GemmPlan& p, int64_t n) {
+  const int64_t groups = ceil_div(ceil_div(n, kTileN), p.waves / p.k_slices);
+  const int64_t whole = p.split > 1 ? p.whole_groups : groups;
+  return whole + (groups - whole) * (p.split > 1 ? p.split : 0);
+}
+
+bool plan_mlp(int fmt_up, int64_t n_up, int64_t k_up, int fmt_dn, int64_t n_dn, int64_t k_dn, int m,
+              const MlpOverride& o, MlpPlan* p) {
+  if (o.fused < 0 || o.fused > 2 || o.down_depth < 0 || o.stream_after < -1) return false;
+  if (n_up % (2 * kTileN) || k_dn != n_up / 2) return false;
+  LaunchOverride up_o, dn_o;
+  up_o.epilogue = kEpiSwiglu;
+  if (!plan_gemm(fmt_up, n_up, k_up, m, up_o, &p->up)) return false;
+  if (!plan_gemm(fmt_dn, n_dn, k_dn, m, dn_o, &p->down)) return false;
+  // The one-launch form: one workgroup size for both halves, and a
+  // consumer that stages all of its K range before it streams (the h
+  // staging waits for the producers; a ring stage would wait once per
+  // unit). The kernels exist for NVFP4 with producer depths 2 and 3 and
+  // consumer depths 2, 3, 4, 6 and 8.
+  up_o.waves = kMlpWaves;
+  dn_o.waves = kMlpWaves;
+  dn_o.x_stage = kStageFull;
+  dn_o.depth = o.down_depth;
+  // Automatic: one launch for a single row only; with more rows the one
+  // workgroup size costs gate_up its tuned shape (at 2 rows on the 27B
+  // shapes: 36.0 against 31.1 us for the two launches).
+  p->fusable = fmt_up == kFmtNvfp4 && fmt_dn == kFmtNvfp4 && (o.fused == 1 || (o.fused == 0 && m == 1)) &&
+               plan_gemm(fmt_up, n_up, k_up, m, up_o, &p->up_fused) &&
+               plan_gemm(fmt_dn, n_dn, k_dn, m, dn_o, &p->down_fused) && p->up_fused.dot_rows == 0 &&
+               (p->up_fused.depth == 2 || p->up_fused.depth == 3) &&
+               (p->up_fused.x_stage == kStageFull || ring_pieces(kMlpWaves, p->up_fused.k_slices, m) == 1) &&
+               p->down_fused.dot_rows == 0 && p->down_fused.block_cols == 0 &&
+               (p->down_fused.depth == 2 || p->down_fused.depth == 3 || p->down_fused.depth == 4 ||
+                p->down_fused.depth == 6 || p->down_fused.depth == 8);
+  if (o.fused == 1 && !p->fusable) return false;
+  p->fused_requested = o.fused == 1;
+  if (!p->fusable) {
+    p->up_fused = p->up;
+    p->down_fused = p->down;
+  }
+  p->producers = static_cast<int>(gemm_grid(p->up_fused, n_up));
+  p->consumers = static_cast<int>(gemm_grid(p->down_fused, n_dn));
+  // Consumers start streaming once most producers are done: the producers'
+  // last workgroups leave CUs idle that the consumers' first units fill.
+  p->stream_after = o.stream_after == -1 ? 0 : o.stream_after > 0 ? o.stream_after : p->producers / 2;
+  if (p->stream_after > p->producers) p->stream_after = p->producers;
+  p->lds_bytes = p->up_fused.lds_bytes > p->down_fused.lds_bytes ? p->up_fused.lds_bytes : p->down_fused.lds_bytes;
+  const auto round256 = [](size_t b) { return (b + 255) & ~size_t(255); };
+  const size_t up_ws = round256(p->up.workspace_bytes > p->up_fused.workspace_bytes ? p->up.workspace_bytes
+                                                                                      : p->up_fused.workspace_bytes);
+  const size_t dn_ws = round256(p->down.workspace_bytes > p->down_fused.workspace_bytes
+                                    ? p->down.workspace_bytes
+                                    : p->down_fused.workspace_bytes);
+  p->down_ws_offset = up_ws;
+  p->flags_offset = up_ws + dn_ws;
+  p->counter_offset = p->flags_offset + static_cast<size_t>(p->consumers) * kMlpFlagLineBytes;
+  p->workspace_bytes = p->counter_offset + kMlpControlBytes;
+  return true;
+}
+
 }  // namespace qpn

@@ -84,6 +84,47 @@ struct GemmPlan {
   size_t workspace_bytes;
 };
 
+// The MLP of a decoder layer, h = SwiGLU(x W_gu^T), y = h W_dn^T, as one
+// launch: the gate_up workgroups (producers) write h with device-scope
+// stores and count themselves in; the down workgroups (consumers), placed
+// after them in the grid, issue their first weight units once
+// `stream_after` producers have finished and stage h once all have. Every
+// workgroup of the grid must be resident at once (the launcher checks the
+// occupancy), so a consumer's wait never holds a slot a producer needs.
+struct MlpOverride {
+  int fused = 0;         // 0 automatic, 1 one launch (or fail), 2 two launches
+  int down_depth = 0;    // stream depth of the consumers, 0 automatic
+  int stream_after = 0;  // producers finished before consumers stream; 0 automatic, -1 at once
+};
+
+constexpr int kMlpWaves = 8;              // workgroup size of both halves of a fused launch
+constexpr size_t kMlpControlBytes = 256;  // arrival counter and status word, padded
+constexpr size_t kMlpFlagLineBytes = 128;  // each consumer's flag line (stream, go), after them
+
+struct MlpPlan {
+  GemmPlan up, down;             // the two-launch plans (each its own tuned shape)
+  GemmPlan up_fused, down_fused; // the one-launch plans (kMlpWaves wavefronts, full-stage consumer)
+  bool fusable;                  // the one-launch plans exist (the launcher still checks occupancy)
+  bool fused_requested;          // the caller asked for one launch
+  int producers, consumers;      // workgroups of the one-launch halves
+  int stream_after;              // resolved: producers finished before consumers stream (0: at once)
+  size_t lds_bytes;              // dynamic LDS of the one-launch kernel
+  // Workspace: the gate_up GEMM's, the down GEMM's (each large enough for
+  // either plan), then the control of the one-launch form: one flag line per
+  // consumer from flags_offset, then the arrival counter and the status word
+  // in the last kMlpControlBytes (from counter_offset).
+  size_t down_ws_offset, flags_offset, counter_offset, workspace_bytes;
+};
+
+// Workgroups in the grid of a GEMM plan for an [n, k] weight.
+int64_t gemm_grid(const GemmPlan& p, int64_t n);
+
+// The MLP of gate_up [n_up, k_up] (gate rows first, then up rows) and down
+// [n_dn, k_dn] with k_dn = n_up / 2, for m activation rows; false when the
+// request is not possible.
+bool plan_mlp(int fmt_up, int64_t n_up, int64_t k_up, int fmt_dn, int64_t n_dn, int64_t k_dn, int m,
+              const MlpOverride& o, MlpPlan* plan);
+
 // x pieces each thread stages per unit in the ring stage.
 int ring_pieces(int waves, int k_slices, int m);
 

@@ -40,6 +40,9 @@ from . import (
     qpn_workspace_bytes,
     qpn_workspace_bytes_tuned,
     make_launch,
+    make_mlp_launch,
+    qpn_mlp,
+    qpn_mlp_workspace_bytes,
 )
 
 
@@ -312,6 +315,44 @@ def gemm_argmax(x, pw, idx=None, val=None, workspace=None, split_k=0, waves=0, d
     qpn_gemm_argmax(x.data_ptr(), d, idx.data_ptr(), val.data_ptr(), m, workspace.data_ptr(),
                     workspace.numel() * workspace.element_size(), launch, _stream())
     return idx, val
+
+
+def mlp_workspace(gate_up, down, m, fused=0, down_depth=0, stream_after=0, device="cuda"):
+    """A zeroed workspace for mlp(gate_up, down) with up to m rows."""
+    launch = make_mlp_launch(fused, down_depth, stream_after)
+    return torch.zeros(qpn_mlp_workspace_bytes(gate_up.desc(), down.desc(), m, launch), dtype=torch.uint8,
+                       device=device)
+
+
+def mlp(x, gate_up, down, h=None, y=None, workspace=None, fused=0, down_depth=0, stream_after=0):
+    """(h, y, launches): h = SwiGLU of x @ dequant(W_gu)^T (fp16 [m, n_gu/2])
+    and y = h @ dequant(W_dn)^T (fp16 [m, n_dn]) through qpn_mlp, in one
+    launch where possible (fused=1: only that, fused=2: two launches);
+    launches is the number of kernels the call enqueued."""
+    m = _activations(x, gate_up)
+    if down.k != gate_up.n // 2:
+        raise ValueError(f"down must have k = {gate_up.n // 2}, not {down.k}")
+    launch = make_mlp_launch(fused, down_depth, stream_after)
+    need = qpn_mlp_workspace_bytes(gate_up.desc(), down.desc(), m, launch)
+    if need == 0:
+        raise QpnError(-2, "qpn_mlp_workspace_bytes")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    h = _output(h, (m, down.k), torch.float16, x, "h")
+    y = _output(y, (m, down.n), torch.float16, x, "y")
+    n = qpn_mlp(x.data_ptr(), gate_up.desc(), down.desc(), h.data_ptr(), y.data_ptr(), m, workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), launch, _stream())
+    return h, y, n
+
+
+def mlp_status(workspace, gate_up, down, m, fused=0, down_depth=0, stream_after=0):
+    """The status word of the control block of a workspace that mlp() used
+    with these arguments (1: a wait of the one-launch form ran past its
+    bound; that call's results are undefined). Reads device memory, so it
+    synchronizes."""
+    need = qpn_mlp_workspace_bytes(gate_up.desc(), down.desc(), m, make_mlp_launch(fused, down_depth, stream_after))
+    word = workspace.view(torch.uint8)[need - 256 + 8: need - 256 + 12]
+    return int(word.cpu().view(torch.int32)[0])
 
 
 def read_ceiling(buf, grid=0, sink=None, loads=0):

@@ -34,7 +34,8 @@ int main(void) {
       (entry_fn)qpn_gemm_plan,          (entry_fn)qpn_gemm_swiglu,
       (entry_fn)qpn_gemm_f32,           (entry_fn)qpn_gemm_argmax,
       (entry_fn)qpn_read_ceiling,       (entry_fn)qpn_read_ceiling_grid,
-      (entry_fn)qpn_gemm_noalloc,
+      (entry_fn)qpn_gemm_noalloc,       (entry_fn)qpn_mlp,
+      (entry_fn)qpn_mlp_workspace_bytes,
   };
   size_t i;
   for (i = 0; i < sizeof entries / sizeof entries[0]; ++i)
@@ -49,6 +50,8 @@ int main(void) {
   printf("sizeof_launch %d\n", (int)sizeof(qpn_launch));
   printf("offset_launch_whole_groups %d\n", (int)offsetof(qpn_launch, whole_groups));
   printf("offset_launch_block_columns %d\n", (int)offsetof(qpn_launch, block_columns));
+  printf("sizeof_mlp_launch %d\n", (int)sizeof(qpn_mlp_launch));
+  printf("offset_mlp_launch_stream_after %d\n", (int)offsetof(qpn_mlp_launch, stream_after));
   printf("max_m %d\n", QPN_MAX_M);
 
   if (strcmp(qpn_status_string(QPN_OK), "ok") != 0) FAIL("status string");

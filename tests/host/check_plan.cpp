@@ -290,12 +290,99 @@ void sweep_entry_points() {
       }
 }
 
+// The fused MLP plans: both halves' plans valid, a one-launch form only with
+// one workgroup size and a full-stage consumer, the workspace regions in
+// order and large enough for either form.
+void sweep_mlp() {
+  const int64_t fs[] = {-16, 0, 16, 32, 48, 1000, 1024, 4352, 8704, 17408, int64_t(1) << 24};
+  const int64_t ks[] = {-16, 0, 16, 256, 272, 5120, int64_t(1) << 20};
+  const int64_t ns[] = {-1, 0, 1, 17, 512, 5120, 151936};
+  const int fused[] = {0, 1, 2, 3, -1};
+  const int depths[] = {0, 0, 2, 3, 4, 6, 8, 5};
+  const int after[] = {0, 0, -1, 1, 160, 100000, -2};
+  for (int it = 0; it < 200000; ++it) {
+    const int64_t f = pick(fs), k = pick(ks), n = pick(ns);
+    const int fmt_up = pick(kFmts), fmt_dn = pick(kFmts);
+    const int m = static_cast<int>(next_u64() % 19) - 1;
+    MlpOverride mo;
+    mo.fused = pick(fused);
+    mo.down_depth = pick(depths);
+    mo.stream_after = pick(after);
+    const int64_t n_up = 2 * f, k_dn = next_u64() % 16 ? f : f + 16;
+    MlpPlan p;
+    memset(&p, 0x5a, sizeof p);
+    ++g_calls;
+    if (!plan_mlp(fmt_up, n_up, k, fmt_dn, n, k_dn, m, mo, &p)) continue;
+    ++g_plans;
+    const LaunchOverride o{};  // for the failure message only
+    const int fmt = fmt_up;
+    REQUIRE(k_dn == n_up / 2 && n_up % 32 == 0 && m >= 1 && m <= kMaxM);
+    REQUIRE(p.up.epilogue == kEpiSwiglu && p.down.epilogue == kEpiNone);
+    if (p.fusable) {
+      REQUIRE(fmt_up == kFmtNvfp4 && fmt_dn == kFmtNvfp4 && mo.fused != 2);
+      REQUIRE(p.up_fused.waves == kMlpWaves && p.down_fused.waves == kMlpWaves);
+      REQUIRE(p.down_fused.x_stage == kStageFull && p.down_fused.dot_rows == 0 && p.down_fused.block_cols == 0);
+      REQUIRE(p.up_fused.depth == 2 || p.up_fused.depth == 3);
+      REQUIRE(p.up_fused.x_stage == kStageFull || ring_pieces(kMlpWaves, p.up_fused.k_slices, m) == 1);
+      if (mo.down_depth) REQUIRE(p.down_fused.depth == mo.down_depth);
+      REQUIRE(p.producers == gemm_grid(p.up_fused, n_up) && p.consumers == gemm_grid(p.down_fused, n));
+      REQUIRE(p.lds_bytes >= p.up_fused.lds_bytes && p.lds_bytes >= p.down_fused.lds_bytes);
+      REQUIRE(p.lds_bytes <= kLdsBudget);
+      REQUIRE(p.stream_after >= 0 && p.stream_after <= p.producers);
+    } else {
+      REQUIRE(mo.fused != 1);
+    }
+    REQUIRE(p.fused_requested == (mo.fused == 1));
+    REQUIRE(p.down_ws_offset % 256 == 0 && p.flags_offset % 256 == 0);
+    REQUIRE(p.down_ws_offset >= p.up.workspace_bytes && p.down_ws_offset >= p.up_fused.workspace_bytes);
+    REQUIRE(p.flags_offset - p.down_ws_offset >= p.down.workspace_bytes);
+    REQUIRE(p.flags_offset - p.down_ws_offset >= p.down_fused.workspace_bytes);
+    REQUIRE(p.counter_offset == p.flags_offset + static_cast<size_t>(p.consumers) * kMlpFlagLineBytes);
+    REQUIRE(p.workspace_bytes == p.counter_offset + kMlpControlBytes);
+  }
+  // the C entry points around it, with arbitrary arguments
+  for (int it = 0; it < 100000; ++it) {
+    qpn_weight up{}, dn{};
+    up.format = pick(kFmts);
+    dn.format = pick(kFmts);
+    up.n = 2 * pick(fs);
+    up.k = pick(ks);
+    dn.n = pick(ns);
+    dn.k = next_u64() % 8 ? up.n / 2 : pick(fs);
+    up.packed = fake_ptr(static_cast<int>(next_u64() % 5));
+    dn.packed = fake_ptr(static_cast<int>(next_u64() % 5));
+    up.tensor_scale = dn.tensor_scale = 1.0f;
+    up.row_scales = dn.row_scales = static_cast<const float*>(fake_ptr(4));
+    qpn_mlp_launch l{};
+    l.fused = pick(fused);
+    l.down_depth = pick(depths);
+    l.stream_after = pick(after);
+    l.reserved = next_u64() % 16 == 0;
+    const int32_t m = static_cast<int32_t>(next_u64() % 19) - 1;
+    const size_t need = qpn_mlp_workspace_bytes(&up, &dn, m, next_u64() % 2 ? &l : nullptr);
+    MlpOverride mo;
+    bool run = false;
+    qpn_status st = QPN_ERR_INVALID_ARG;
+    MlpPlan p;
+    if (to_mlp_override(&l, &mo))
+      st = check_mlp(fake_ptr(static_cast<int>(next_u64() % 5)), &up, &dn, fake_ptr(static_cast<int>(next_u64() % 5)),
+                     fake_ptr(static_cast<int>(next_u64() % 5)), m, fake_ptr(static_cast<int>(next_u64() % 5)),
+                     next_u64() % 2 ? need : need / 2, mo, &p, &run);
+    g_calls += 2;
+    if (st != QPN_OK && run) {
+      printf("FAIL check_mlp: a failed check asks for a launch\n");
+      exit(1);
+    }
+  }
+}
+
 }  // namespace
 
 int main() {
   sweep_planner();
   sweep_checks();
   sweep_entry_points();
+  sweep_mlp();
   printf("ok %ld %ld\n", g_plans, g_calls);
   return 0;
 }

@@ -61,6 +61,8 @@ def test_header_compiles_as_c99_and_links(tmp_path):
     assert int(got["sizeof_launch"]) == ctypes.sizeof(q.qpn_launch)
     assert int(got["offset_launch_whole_groups"]) == q.qpn_launch.whole_groups.offset
     assert int(got["offset_launch_block_columns"]) == q.qpn_launch.block_columns.offset
+    assert int(got["sizeof_mlp_launch"]) == ctypes.sizeof(q.qpn_mlp_launch)
+    assert int(got["offset_mlp_launch_stream_after"]) == q.qpn_mlp_launch.stream_after.offset
     assert int(got["max_m"]) == q.QPN_MAX_M
     w = _w(n=34816, k=5120)
     p = q.qpn_gemm_plan(w, 1)
@@ -499,3 +501,57 @@ def test_noalloc_checks_before_any_device_call():
     assert lib.qpn_gemm_noalloc(FAKE, None, FAKE, 1, None) == q.QPN_ERR_INVALID_ARG
     assert lib.qpn_gemm_noalloc(FAKE, ctypes.byref(_w(fmt=9)), FAKE, 1, None) == q.QPN_ERR_INVALID_ARG
     assert lib.qpn_gemm_noalloc(None, ctypes.byref(_w()), FAKE, 0, None) == q.QPN_OK  # nothing to do
+
+
+def _mlp_weights(f=17408, k=5120, n=5120, fmt_up=None, fmt_dn=None):
+    fu = fmt_up or q.QPN_FMT_NVFP4
+    fd = fmt_dn or q.QPN_FMT_NVFP4
+    return q.make_weight(fu, 2 * f, k, FAKE, 1.0, FAKE), q.make_weight(fd, n, f, FAKE, 1.0, FAKE)
+
+
+def _mlp(x, up, dn, h, y, m, ws, ws_bytes, launch=None):
+    n = ctypes.c_int32(-1)
+    st = q.lib().qpn_mlp(x, ctypes.byref(up), ctypes.byref(dn), h, y, m, ws, ws_bytes,
+                         ctypes.byref(launch) if launch is not None else None, ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_mlp_workspace_layout():
+    """The two GEMMs' workspaces (each sized for either form) and a 256-byte
+    control block at the end; the one-launch form exists for NVFP4 only."""
+    up, dn = _mlp_weights()
+    for m in (1, 2, 4, 8, 16):
+        need = q.qpn_mlp_workspace_bytes(up, dn, m)
+        ws_up = max(q.qpn_workspace_bytes_tuned(up, m, q.make_launch(epilogue=q.QPN_EPILOGUE_SWIGLU)),
+                    q.qpn_workspace_bytes_tuned(up, m, q.make_launch(epilogue=q.QPN_EPILOGUE_SWIGLU,
+                                                                     waves_per_group=8)))
+        assert need >= (ws_up + 255) // 256 * 256 + 256
+        assert need % 256 == 0
+        assert q.qpn_mlp_workspace_bytes(up, dn, m, q.make_mlp_launch(fused=2)) > 0
+    f8_up, f8_dn = _mlp_weights(fmt_up=q.QPN_FMT_FP8_E4M3)
+    assert q.qpn_mlp_workspace_bytes(f8_up, f8_dn, 1, q.make_mlp_launch(fused=1)) == 0
+    assert q.qpn_mlp_workspace_bytes(f8_up, f8_dn, 1) > 0
+
+
+def test_mlp_argument_checks():
+    """Rejected before any device work (no GPU here)."""
+    up, dn = _mlp_weights()
+    need = q.qpn_mlp_workspace_bytes(up, dn, 1)
+    assert _mlp(FAKE, up, dn, FAKE, FAKE, 1, FAKE, need - 16)[0] == q.QPN_ERR_BUFFER_TOO_SMALL
+    assert _mlp(FAKE, up, dn, FAKE, FAKE, 1, None, need)[0] == q.QPN_ERR_INVALID_ARG
+    assert _mlp(FAKE, up, dn, FAKE + 8, FAKE, 1, FAKE, need)[0] == q.QPN_ERR_INVALID_ARG   # h alignment
+    assert _mlp(FAKE + 2, up, dn, FAKE, FAKE, 1, FAKE, need)[0] == q.QPN_ERR_INVALID_ARG   # x alignment
+    assert _mlp(FAKE, up, dn, FAKE, FAKE + 1, 1, FAKE, need)[0] == q.QPN_ERR_INVALID_ARG   # y alignment
+    assert _mlp(FAKE, up, dn, FAKE, FAKE, 17, FAKE, need)[0] == q.QPN_ERR_INVALID_ARG
+    assert _mlp(FAKE, up, dn, FAKE, FAKE, 0, FAKE, need) == (q.QPN_OK, 0)                 # nothing to do
+    bad_up, bad_dn = _mlp_weights()
+    bad_dn.k = 17392                                                                     # k != n_up / 2
+    assert _mlp(FAKE, bad_up, bad_dn, FAKE, FAKE, 1, FAKE, need)[0] == q.QPN_ERR_INVALID_ARG
+    for launch in (q.make_mlp_launch(fused=3), q.make_mlp_launch(down_depth=5),
+                   q.make_mlp_launch(stream_after=-2), q.qpn_mlp_launch(0, 0, 0, 1)):
+        assert _mlp(FAKE, up, dn, FAKE, FAKE, 1, FAKE, need, launch)[0] == q.QPN_ERR_INVALID_ARG
+    f8_up, f8_dn = _mlp_weights(fmt_up=q.QPN_FMT_FP8_E4M3)
+    need8 = q.qpn_mlp_workspace_bytes(f8_up, f8_dn, 1)
+    assert _mlp(FAKE, f8_up, f8_dn, FAKE, FAKE, 1, FAKE, need8, q.make_mlp_launch(fused=1))[0] == \
+        q.QPN_ERR_UNSUPPORTED
+

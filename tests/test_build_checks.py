@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = qbuild.CSRC
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = qbuild.HIPCC
-DEVICE_SOURCES = ["qpn_gemm.hip", "qpn_pack.hip", "qpn_api.hip"]
+DEVICE_SOURCES = ["qpn_gemm.hip", "qpn_mlp.hip", "qpn_pack.hip", "qpn_api.hip"]
 HOST_ONLY_SOURCES = ["qpn_plan.cpp", "qpn_checks.cpp"]
 
 # hipcc flags of the library build minus the output kind
