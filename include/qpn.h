@@ -367,12 +367,11 @@ qpn_status qpn_gemm_argmax(const void* x_dev, const qpn_weight* w, int32_t* idx_
 
 /*
  * The MLP of a decoder layer: h = SwiGLU(x W_gate^T, x W_up^T) as in
- * qpn_gemm_swiglu, then y = h W_down^T as in qpn_gemm, in ONE launch where
- * possible ([P3] "What I actually built": the dense layer's gate_up and down
- * projections, streamed back to back). In that launch the down workgroups
- * start streaming their weights while the last gate_up workgroups still run
- * and read h as soon as all of it is written, so the chip does not idle
- * between the two GEMMs.
+ * qpn_gemm_swiglu, then y = h W_down^T as in qpn_gemm ([P3] "What I actually
+ * built": the dense layer's gate_up and down projections, streamed back to
+ * back), as two GEMM launches or, on request, as ONE launch in which the
+ * down workgroups start streaming their weights while the last gate_up
+ * workgroups still run and read h as soon as all of it is written.
  *   gate_up   [W_gate; W_up], n = 2 * F (F a multiple of 16), k = K.
  *   down      n = N, k = F.
  *   x_dev     fp16 [m][K], 16-byte aligned.
@@ -381,13 +380,17 @@ qpn_status qpn_gemm_argmax(const void* x_dev, const qpn_weight* w, int32_t* idx_
  *   y_dev     fp16 [m][N] output (as qpn_gemm on h), 2-byte aligned.
  *   launch    NULL (automatic) or a launch shape; `launches` (host, may be
  *             NULL) gets the number of kernels enqueued, 1 or 2.
- * The one-launch form needs NVFP4 weights and a grid that fits on the
- * device at once (the call checks the occupancy; the down workgroups stage
- * their K range of h whole, so more rows cut down's K into more ranges and
- * enlarge the grid); otherwise the call enqueues the two GEMMs (or, with
- * launch->fused = 1, returns QPN_ERR_UNSUPPORTED). Both forms are within the
- * GEMMs' bounds; where their launch shapes agree (the 27B shapes at m = 1)
- * they give the same bits. The workspace is
+ * Automatic is two launches: on the 27B shapes the one launch measured
+ * level with them at m = 1 and slower at m = 2. The one-launch form
+ * (launch->fused = 1) needs NVFP4 weights and a grid that fits on the device
+ * at once (the call checks the occupancy; the down workgroups stage their K
+ * range of h whole, so more rows cut down's K into more ranges and enlarge
+ * the grid), else the call returns QPN_ERR_UNSUPPORTED with nothing
+ * enqueued. Both forms are within the GEMMs' bounds; y is the down GEMM's on
+ * the h the call writes, bit for bit, and where the gate_up launch shapes
+ * agree (the 27B shapes at m = 1) h is too but for rare 1-ulp differences of
+ * the epilogue's fp32 rounding.
+ * The workspace is
  * qpn_mlp_workspace_bytes(gate_up, down, m, launch), 16-byte aligned: the two
  * GEMMs' workspaces, a 128-byte flag line per down workgroup of the
  * one-launch form, and a 256-byte control block at its end (an arrival
@@ -400,8 +403,8 @@ qpn_status qpn_gemm_argmax(const void* x_dev, const qpn_weight* w, int32_t* idx_
  * waits then end the call with the status word set).
  */
 typedef struct {
-  int32_t fused;        /* 0 automatic (one launch at m = 1), 1 one launch or QPN_ERR_UNSUPPORTED,
-                           2 two launches */
+  int32_t fused;        /* 0 automatic (two launches: the faster or equal form as measured),
+                           1 one launch or QPN_ERR_UNSUPPORTED, 2 two launches */
   int32_t down_depth;   /* one launch: weight units in flight per down wavefront: 0 auto, 2, 3, 4, 6, 8 */
   int32_t stream_after; /* one launch: gate_up workgroups finished before the down workgroups issue
                            their first weight units: 0 auto (half of them), -1 at once, else the count */

@@ -1,5 +1,6 @@
 // The MLP of a decoder layer in one launch: h = SwiGLU(x W_gu^T) and
-// y = h W_dn^T, both weights NVFP4 in the packed layout.
+// y = h W_dn^T, both weights NVFP4 in the packed layout (qpn_mlp with
+// launch->fused = 1; its automatic form is the two GEMM launches).
 //
 // Two GEMM launches leave the chip part idle twice: at the end of gate_up,
 // whose last workgroups finish several microseconds after the first, and at
@@ -15,6 +16,16 @@
 // pass over memory: the fusion of the SwiGLU epilogue between gate_up and
 // down that the pages' layer structure implies ([P3] "What I actually built":
 // the dense layer's gate_up and down projections).
+//
+// Measured on the 27B shapes (gate_up 34816 x 5120, down 5120 x 17408) at
+// one row it is level with the two launches, 30.2 against 30.15 us: the
+// signal from the last producer takes 2.5-3 us to reach the consumers (its h
+// stores acknowledged, its arrival returned, the flags raised and polled),
+// about what the second launch and down's own start cost, and down's work
+// after it (staging h, then 17 units per wavefront on 160 CUs) is no shorter
+// for having its first units in flight. Polling one shared counter instead
+// of per-consumer lines made the launch 50% slower; 32 counter replicas
+// polled by a few consumers each were slower than the lines (31.9 us).
 //
 // Progress: the launcher requires that every workgroup of the grid be
 // resident at once (the occupancy of this kernel times the CUs), so the

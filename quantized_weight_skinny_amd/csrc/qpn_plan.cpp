@@ -256,10 +256,12 @@ bool plan_mlp(int fmt_up, int64_t n_up, int64_t k_up, int fmt_dn, int64_t n_dn, 
   dn_o.waves = kMlpWaves;
   dn_o.x_stage = kStageFull;
   dn_o.depth = o.down_depth;
-  // Automatic: one launch for a single row only; with more rows the one
-  // workgroup size costs gate_up its tuned shape (at 2 rows on the 27B
-  // shapes: 36.0 against 31.1 us for the two launches).
-  p->fusable = fmt_up == kFmtNvfp4 && fmt_dn == kFmtNvfp4 && (o.fused == 1 || (o.fused == 0 && m == 1)) &&
+  // Only on request: on the 27B shapes the one launch measured level with
+  // the two at one row (30.2 against 30.15 us; the last producer's signal
+  // takes 2.5-3 us to reach the consumers, about what the second launch
+  // costs) and slower at two rows, where one workgroup size costs gate_up its
+  // tuned shape (36.0 against 31.1 us).
+  p->fusable = fmt_up == kFmtNvfp4 && fmt_dn == kFmtNvfp4 && o.fused == 1 &&
                plan_gemm(fmt_up, n_up, k_up, m, up_o, &p->up_fused) &&
                plan_gemm(fmt_dn, n_dn, k_dn, m, dn_o, &p->down_fused) && p->up_fused.dot_rows == 0 &&
                (p->up_fused.depth == 2 || p->up_fused.depth == 3) &&
