@@ -285,9 +285,10 @@ def _time_matrix(mat, m, reps, swiglu=False, argmax=False, stat="median", label=
     return us, mat.bytes_for(m, swiglu, argmax) / (us * 1e-6) / 1e9
 
 
-def time_mlp(gate_up, down, m, reps=10):
+def time_mlp(gate_up, down, m, reps=10, one_launch=False):
     """The MLP of one layer as the decoder runs it: x -> gate_up with the
-    SwiGLU epilogue -> h -> down -> y, over the rotating copies, one graph.
+    SwiGLU epilogue -> h -> down -> y, over the rotating copies, one graph:
+    as two GEMM launches, or (one_launch) as qpn_mlp's one-launch form.
     Returns (µs per MLP, GB/s over weights + x + h written and read + y)."""
     import torch
     from quantized_weight_skinny_amd import torch_api as qt
@@ -296,9 +297,13 @@ def time_mlp(gate_up, down, m, reps=10):
     y = torch.empty((m, down.n), dtype=torch.float16, device="cuda")
     ws_g = qt.new_workspace(gate_up.copies[0], m, swiglu=True)
     ws_d = qt.new_workspace(down.copies[0], m)
+    ws_f = qt.mlp_workspace(gate_up.copies[0], down.copies[0], m, fused=1) if one_launch else None
     r = min(len(gate_up.copies), len(down.copies))
 
     def mlp(i):
+        if one_launch:
+            qt.mlp(x, gate_up.copies[i], down.copies[i], h=h, y=y, workspace=ws_f, fused=1)
+            return
         qt.gemm_swiglu(x, gate_up.copies[i], out=h, workspace=ws_g)
         qt.gemm(h, down.copies[i], out=y, workspace=ws_d)
 
@@ -307,7 +312,7 @@ def time_mlp(gate_up, down, m, reps=10):
     g = capture([(lambda i=i: mlp(i)) for i in range(r)])
     g.replay()
     torch.cuda.synchronize()
-    us = replay_us(g, r, reps, label=f"nvfp4_m{m}/mlp_swiglu")
+    us = replay_us(g, r, reps, label=f"nvfp4_m{m}/mlp_{'one_launch' if one_launch else 'swiglu'}")
     del g
     nbytes = gate_up.bytes_for(m, swiglu=True) + down.bytes_for(m)
     return us, nbytes / (us * 1e-6) / 1e9
@@ -386,7 +391,8 @@ def read_pair_us(a, b, total=4 << 30, reps=5):
     return us
 
 
-KERNEL_SOURCES = ("qpn_device.hpp", "qpn_gemm.hip", "qpn_internal.hpp", "qpn_plan.hpp", "qpn_plan.cpp")
+KERNEL_SOURCES = ("qpn_device.hpp", "qpn_gemm.hip", "qpn_gemm_body.hpp", "qpn_internal.hpp", "qpn_plan.hpp",
+                  "qpn_plan.cpp")
 
 
 def kernel_source_hash():
@@ -697,6 +703,9 @@ def main():
         for mm in (1, 8):
             per[f"nvfp4_m{mm}/gate_up_swiglu"] = time_matrix(gate_up, mm, swiglu=True)
             per[f"nvfp4_m{mm}/mlp_swiglu"] = time_mlp(gate_up, down, mm)
+        # qpn_mlp's one-launch form (on request only: level with the two
+        # launches at one row, slower above)
+        per["nvfp4_m1/mlp_one_launch"] = time_mlp(gate_up, down, 1, one_launch=True)
         del gate_up, down
         torch.cuda.empty_cache()
         for name in ("qkv", "o_proj"):

@@ -270,6 +270,15 @@ __device__ __forceinline__ void fuse_wait(const FuseCtl& ctl, const int* flag) {
   asm volatile("" ::: "memory");
 }
 
+// Four consecutive fp32 partial sums with one 16-byte store under the
+// device-coherent cache policy (sc1, the policy of a relaxed device-scope
+// atomic store): as four 4-byte stores, each one costs a write of its own
+// memory sector, four times the bytes. The caller waits for the store
+// (s_waitcnt) before it publishes the partials.
+__device__ __forceinline__ void store4_coherent(float* p, const f4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+
 // One output pair of SwiGLU values, 4 consecutive fp16 (8 bytes, aligned):
 // with COHERENT a device-scope store (written through to the level all XCDs
 // share), for a consumer in the same launch.
@@ -743,9 +752,13 @@ __device__ __forceinline__ void gemm_body(
   // workgroup issues its loads only after the increment has returned.
   if (owner && mcol < M) {
     float* dst = ws + (static_cast<size_t>(s) * M + mcol) * N;
+    if (N % 4 == 0 && n0 + 3 < N) {
+      store4_coherent(dst + n0, acc);  // 16-byte aligned: N % 4 == 0 and n0 % 4 == 0
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (n0 + r < N) __hip_atomic_store(dst + n0 + r, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int r = 0; r < 4; ++r)
+        if (n0 + r < N) __hip_atomic_store(dst + n0 + r, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
