@@ -74,6 +74,7 @@ __host__ __device__ constexpr int64_t unit_offset(int64_t nt, int64_t u, int64_t
 struct Stream {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t stride;  // bytes from one unit of the tile to the next
+  Stream() = default;  // set up later, with the constructor below
   __device__ __forceinline__ Stream(const uint8_t* base, uint32_t bytes, uint32_t unit_stride)
       : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kRsrcWord3)),
         stride(unit_stride) {}

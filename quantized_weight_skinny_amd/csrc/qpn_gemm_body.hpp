@@ -375,9 +375,19 @@ __device__ __forceinline__ void gemm_body(
   const int nt = swiglu ? (tn < half_tn ? pair : NTh + pair) : grp * TN + tn;
   const bool active = swiglu ? pair < NTh : nt < NT;
   const uint32_t unit_stride = static_cast<uint32_t>(NT) * kBytes;
-  const Stream stream(packed + unit_offset(active ? nt : 0, u0 + wu0, NT, kBytes),
-                      active && wnu > 0 ? static_cast<uint32_t>(wnu - 1) * unit_stride + kBytes : 0u,
-                      unit_stride);
+  // The weight stream is set up where the first weight units are issued:
+  // after the activation loads, behind a scheduling barrier, so that its
+  // address arithmetic (some 30-65 instructions) sits between the two.
+  // Measured on the 27B shapes, the ring launches at 8 rows run 2-5% faster
+  // than with the weight loads issued right behind the activation loads, and
+  // the full stage 2% faster than with the set-up ahead of both. The likely
+  // reason: the activation requests of all the CU's wavefronts then reach the
+  // memory pipeline ahead of the weight requests, so the stage's first
+  // barrier does not wait behind those.
+  auto weight_stream = [&]() {
+    return Stream(packed + unit_offset(active ? nt : 0, u0 + wu0, NT, kBytes),
+                  active && wnu > 0 ? static_cast<uint32_t>(wnu - 1) * unit_stride + kBytes : 0u, unit_stride);
+  };
 
   // B-operand column m of the MFMA is activation row m. Lanes of columns
   // m >= M read row M-1 (an LDS broadcast); their output columns are never
@@ -399,6 +409,7 @@ __device__ __forceinline__ void gemm_body(
   // and move their loads across the staging barriers, which would both delay
   // the stream and break the staging waits.)
   Unit<FMT> buf[DEPTH];
+  Stream stream;
 
   if constexpr (XP == 0) {
     // Full stage: this K range of every activation row goes to LDS before
@@ -434,6 +445,7 @@ __device__ __forceinline__ void gemm_body(
       // device-coherent loads. Both flags of the line are then cleared for
       // the next call: no producer writes them again in this launch (the
       // stream flag was seen raised before the go flag was awaited).
+      stream = weight_stream();
       const int* line = ctl.flags + static_cast<size_t>(block) * kFuseFlagInts;
       if (ctl.stream_after > 0) fuse_wait(ctl, line);
 #pragma unroll
@@ -464,6 +476,8 @@ __device__ __forceinline__ void gemm_body(
         if (c0 + lane < live_chunks)
           lds_dma16(x + static_cast<size_t>(m) * K + kbase + (c0 + lane) * 8, xs + m * stride + c0 * 8);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      stream = weight_stream();
 
       // Then issue the first DEPTH units of the weight stream unit by unit, in
       // the order the loop will consume them.
@@ -592,6 +606,8 @@ __device__ __forceinline__ void gemm_body(
     u4 xr[DEPTH][XP];
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) load_x(xr[i], i);
+    __builtin_amdgcn_sched_barrier(0);
+    stream = weight_stream();
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
       load_unit(buf[i], stream, i, lane);
