@@ -36,10 +36,12 @@ constexpr TunedLaunch kTuned[] = {
     // tiles fill the 256 CUs evenly (256 or 512 groups); the last 16 (32)
     // groups split K four ways, a short tail of small workgroups. At M = 2
     // the full stage beats the ring (18.5 against 19.4 us, alternated runs).
+    // From 5 rows on, groups of 8 tiles (320 workgroups) beat groups of 4
+    // (640): 19.80 against 19.94 us at M = 8, 19.50 against 19.99 with the
+    // SwiGLU epilogue, 22.43 against 22.96 at M = 16 (ten alternated rounds).
     {kFmtNvfp4, 34816, 5120, 1, 8, 1, 4, 2, kStageRing, 256},
     {kFmtNvfp4, 34816, 5120, 2, 4, 1, 4, 2, kStageFull, 512},
-    {kFmtNvfp4, 34816, 5120, 4, 8, 1, 4, 2, kStageRing, 256},
-    {kFmtNvfp4, 34816, 5120, 16, 4, 1, 4, 2, kStageRing, 512},
+    {kFmtNvfp4, 34816, 5120, 16, 8, 1, 4, 2, kStageRing, 256},
     // NVFP4 down 5120 x 17408
     {kFmtNvfp4, 5120, 17408, 2, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 17408, 4, 8, 2, 3, 2},
     {kFmtNvfp4, 5120, 17408, 8, 8, 2, 3, 2, kStageRing}, {kFmtNvfp4, 5120, 17408, 16, 8, 2, 3, 2, kStageRing},
