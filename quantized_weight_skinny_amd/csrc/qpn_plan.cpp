@@ -42,8 +42,9 @@ constexpr TunedLaunch kTuned[] = {
     {kFmtNvfp4, 34816, 5120, 1, 8, 1, 4, 2, kStageRing, 256},
     {kFmtNvfp4, 34816, 5120, 2, 4, 1, 4, 2, kStageFull, 512},
     {kFmtNvfp4, 34816, 5120, 16, 8, 1, 4, 2, kStageRing, 256},
-    // NVFP4 down 5120 x 17408
-    {kFmtNvfp4, 5120, 17408, 2, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 17408, 4, 8, 2, 3, 2},
+    // NVFP4 down 5120 x 17408 (at M = 3 and 4 the ring at depth 3 measured 12.43 / 12.48 us
+    // against 12.45 / 12.68 for the full stage at depth 2, eight alternated rounds)
+    {kFmtNvfp4, 5120, 17408, 2, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 17408, 4, 8, 2, 3, 3, kStageRing},
     {kFmtNvfp4, 5120, 17408, 8, 8, 2, 3, 2, kStageRing}, {kFmtNvfp4, 5120, 17408, 16, 8, 2, 3, 2, kStageRing},
     // NVFP4 qkv 7168 x 5120 and o_proj 5120 x 5120
     {kFmtNvfp4, 7168, 5120, 4, 8, 4, 1, 3}, {kFmtNvfp4, 7168, 5120, 8, 8, 4, 1, 2, kStageRing},
@@ -60,10 +61,13 @@ constexpr TunedLaunch kTuned[] = {
     {kFmtNvfp4, 8704, 5120, 1, 8, 2, 1, 3}, {kFmtNvfp4, 8704, 5120, 8, 4, 2, 6, 2, kStageRing, 256},
     {kFmtNvfp4, 5120, 4352, 1, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 4352, 8, 8, 4, 1, 2},
     // FP8 qkv 7168 x 5120
-    {kFmtFp8, 7168, 5120, 2, 4, 2, 1, 2}, {kFmtFp8, 7168, 5120, 4, 4, 2, 1, 3, kStageRing},
+    // (M = 2 takes the ring of M = 4: 8.60 against 8.70 us for the full stage, alternated rounds)
+    {kFmtFp8, 7168, 5120, 1, 4, 2, 1, 2}, {kFmtFp8, 7168, 5120, 4, 4, 2, 1, 3, kStageRing},
     {kFmtFp8, 7168, 5120, 8, 4, 2, 1, 2, kStageRing}, {kFmtFp8, 7168, 5120, 16, 8, 2, 2, 2, kStageRing},
     // FP8 o_proj 5120 x 5120
-    {kFmtFp8, 5120, 5120, 1, 4, 2, 1, 3}, {kFmtFp8, 5120, 5120, 2, 4, 2, 1, 4},
+    // (M = 1 at depth 2: 7.18 against 7.27 us at depth 3; M = 2 takes the ring of M = 3..8: 7.43
+    // against 7.65 for the full stage at depth 4; alternated rounds)
+    {kFmtFp8, 5120, 5120, 1, 4, 2, 1, 2},
     {kFmtFp8, 5120, 5120, 8, 4, 2, 1, 3, kStageRing}, {kFmtFp8, 5120, 5120, 16, 8, 2, 3, 2, kStageRing},
     // FP8 down 5120 x 17408
     {kFmtFp8, 5120, 17408, 1, 8, 4, 1, 2}, {kFmtFp8, 5120, 17408, 4, 4, 1, 3, 3, kStageRing},

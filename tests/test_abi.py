@@ -205,7 +205,8 @@ def test_plan_resolves_tuned_and_rule_based_launches():
     assert _plan(_w(n=1000, k=3072), 8).x_stage == ring
     # the tuned table picks stages per shape and row count
     assert _plan(_w(n=151936, k=5120), 8).x_stage == ring
-    assert _plan(_w(n=5120, k=17408), 4).x_stage == full
+    assert _plan(_w(n=5120, k=17408), 4).x_stage == ring
+    assert _plan(_w(n=5120, k=17408), 2).x_stage == full
     # an automatic stage falls back to what the other fields allow
     assert _plan(_w(n=1000, k=3072), 8, depth=6).x_stage == full
     assert _plan(_w(n=1000, k=3072), 16, waves_per_group=4, k_slices=4).x_stage == full
