@@ -78,10 +78,11 @@ hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, c
   const int groups = static_cast<int>(ceil_div(NT, WAVES / p.k_slices));
   const int whole = p.split > 1 ? p.whole_groups : groups;  // groups that take all of K
   const unsigned grid = static_cast<unsigned>(whole + (groups - whole) * (p.split > 1 ? p.split : 0));
-  // Dynamic LDS above the 64 KiB default must be allowed per kernel.
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH, EPI, XP, DOT>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBudget));
+  // Dynamic LDS above the 64 KiB default must be allowed per kernel and device.
+  static std::atomic<uint64_t> lds_allowed{0};
+  const hipError_t attr = allow_dynamic_lds(
+      reinterpret_cast<const void*>(&gemm_kernel<FMT, WAVES, DEPTH, EPI, XP, DOT>), static_cast<int>(kLdsBudget),
+      lds_allowed);
   if (attr != hipSuccess) return attr;
   char* wsb = static_cast<char*>(workspace);
   int* counters = p.split > 1 ? reinterpret_cast<int*>(wsb) : nullptr;

@@ -5,9 +5,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "qpn_plan.hpp"
 
 namespace qpn {
+
+// Allow `fn` dynamic LDS up to `bytes` on the current device. The attribute
+// belongs to the device, so it is set once per kernel and device: `done` (one
+// per kernel) records devices 0..63; any other device sets it on every call.
+// A failed call is not recorded and is tried again next time.
+inline hipError_t allow_dynamic_lds(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const hipError_t set = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (set == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return set;
+}
 
 
 // y: fp16 output (or int32 indices for the argmax epilogue); val: the

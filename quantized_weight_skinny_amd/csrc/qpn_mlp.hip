@@ -134,8 +134,8 @@ template <int DA, int XPA, int DB>
 hipError_t launch_fused(const MlpPlan& p, const HalfArgs& a, const HalfArgs& b, const FuseCtl& ctl,
                         hipStream_t stream) {
   const void* fn = reinterpret_cast<const void*>(&mlp_kernel<kFmtNvfp4, DA, XPA, DB>);
-  static const hipError_t attr =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBudget));
+  static std::atomic<uint64_t> lds_allowed{0};
+  const hipError_t attr = allow_dynamic_lds(fn, static_cast<int>(kLdsBudget), lds_allowed);
   if (attr != hipSuccess) return attr;
   int per_cu = 0;
   const hipError_t occ =
