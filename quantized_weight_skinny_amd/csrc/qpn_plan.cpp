@@ -120,13 +120,17 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   // head it measured the same as few, wide groups, 70.2 against 70.4 us at
   // M = 1 and 70.1 against 70.2 at M = 8).
   LaunchOverride w = o;
+  int tuned_tn = 0;  // n-tiles per workgroup behind a tabled whole_groups (0: none tabled)
   if (const TunedLaunch* t = find_tuned(fmt, n, k, m)) {
     if (!w.split) w.split = t->split;
     if (!w.waves) w.waves = t->waves;
     if (!w.k_slices) w.k_slices = t->k_slices;
     if (!w.depth) w.depth = t->depth;
     if (!w.x_stage) w.x_stage = t->x_stage;
-    if (!w.whole_groups && !o.split) w.whole_groups = t->whole_groups;
+    if (!w.whole_groups && !o.split && t->whole_groups) {
+      w.whole_groups = t->whole_groups;
+      tuned_tn = t->waves / t->k_slices;
+    }
   }
 
   // K ranges over workgroups: as few as a full activation stage allows.
@@ -174,8 +178,12 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   if (o.valu_dot && (o.epilogue != kEpiNone || depth > 4 || m > 4 || o.x_stage == kStageRing)) return false;
 
   // Groups kept whole (split > 1 only): a whole group's workgroup covers
-  // all KU units, so a full stage must hold them.
+  // all KU units, so a full stage must hold them. A tabled count was chosen
+  // for the table's n-tiles per workgroup; where the caller changed those,
+  // it is scaled to keep the same n-tiles whole (the balanced grid).
   const int64_t groups = ceil_div(NT, waves / ks);
+  if (tuned_tn && waves / ks != tuned_tn)
+    w.whole_groups = static_cast<int>(static_cast<int64_t>(w.whole_groups) * tuned_tn / (waves / ks));
   const int64_t whole = split > 1 ? (w.whole_groups < groups ? w.whole_groups : groups) : groups;
   if (w.whole_groups < 0) return false;
 
@@ -263,11 +271,10 @@ bool plan_mlp(int fmt_up, int64_t n_up, int64_t k_up, int fmt_dn, int64_t n_dn, 
   dn_o.waves = kMlpWaves;
   dn_o.x_stage = kStageFull;
   dn_o.depth = o.down_depth;
-  // Only on request: on the 27B shapes the one launch measured level with
-  // the two at one row (30.2 against 30.15 us; the last producer's signal
-  // takes 2.5-3 us to reach the consumers, about what the second launch
-  // costs) and slower at two rows, where one workgroup size costs gate_up its
-  // tuned shape (36.0 against 31.1 us).
+  // Only on request: on the 27B shapes the one launch measures level with
+  // the two (M = 1: 30.29 against 29.94 us, M = 2: 30.66 against 30.97; the
+  // last producer's signal takes 2.5-3 us to reach the consumers, about what
+  // the second launch costs).
   p->fusable = fmt_up == kFmtNvfp4 && fmt_dn == kFmtNvfp4 && o.fused == 1 &&
                plan_gemm(fmt_up, n_up, k_up, m, up_o, &p->up_fused) &&
                plan_gemm(fmt_dn, n_dn, k_dn, m, dn_o, &p->down_fused) && p->up_fused.dot_rows == 0 &&
