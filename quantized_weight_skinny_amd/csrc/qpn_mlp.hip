@@ -12,20 +12,22 @@
 // device-coherent loads) only once every producer has counted itself in after
 // its h stores (device-scope, written through to the level all XCDs share)
 // were acknowledged. The producers whose arrival completes a stage raise a
-// flag in each consumer's own line, which only that consumer polls. This is the dependency of the two GEMMs, with no extra
-// pass over memory: the fusion of the SwiGLU epilogue between gate_up and
-// down that the pages' layer structure implies ([P3] "What I actually built":
-// the dense layer's gate_up and down projections).
+// flag in each consumer's own line, which only that consumer polls. This is
+// the dependency of the two GEMMs, with no extra pass over memory: the fusion
+// of the SwiGLU epilogue between gate_up and down that the pages' layer
+// structure implies ([P3] "What I actually built": the dense layer's gate_up
+// and down projections).
 //
-// Measured on the 27B shapes (gate_up 34816 x 5120, down 5120 x 17408) at
-// one row it is level with the two launches, 30.2 against 30.15 us: the
-// signal from the last producer takes 2.5-3 us to reach the consumers (its h
-// stores acknowledged, its arrival returned, the flags raised and polled),
-// about what the second launch and down's own start cost, and down's work
-// after it (staging h, then 17 units per wavefront on 160 CUs) is no shorter
-// for having its first units in flight. Polling one shared counter instead
-// of per-consumer lines made the launch 50% slower; 32 counter replicas
-// polled by a few consumers each were slower than the lines (31.9 us).
+// Measured on the 27B shapes (gate_up 34816 x 5120, down 5120 x 17408) it is
+// level with the two launches (one row: 30.2 against 30.15 us; two rows:
+// 30.66 against 30.97): the signal from the last producer takes 2.5-3 us to
+// reach the consumers (its h stores acknowledged, its arrival returned, the
+// flags raised and polled), about what the second launch and down's own
+// start cost, and down's work after it (staging h, then 17 units per
+// wavefront on 160 CUs) is no shorter for having its first units in flight.
+// Polling one shared counter instead of per-consumer lines made the launch
+// 50% slower; 32 counter replicas polled by a few consumers each were slower
+// than the lines (31.9 us).
 //
 // Progress: the launcher requires that every workgroup of the grid be
 // resident at once (the occupancy of this kernel times the CUs), so the
