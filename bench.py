@@ -704,8 +704,11 @@ def main():
             per[f"nvfp4_m{mm}/gate_up_swiglu"] = time_matrix(gate_up, mm, swiglu=True)
             per[f"nvfp4_m{mm}/mlp_swiglu"] = time_mlp(gate_up, down, mm)
         # qpn_mlp's one-launch form (on request only: level with the two
-        # launches at one row, slower above)
+        # launches at one and two rows), with the two-launch form at two rows
+        # beside it
         per["nvfp4_m1/mlp_one_launch"] = time_mlp(gate_up, down, 1, one_launch=True)
+        per["nvfp4_m2/mlp_swiglu"] = time_mlp(gate_up, down, 2)
+        per["nvfp4_m2/mlp_one_launch"] = time_mlp(gate_up, down, 2, one_launch=True)
         del gate_up, down
         torch.cuda.empty_cache()
         for name in ("qkv", "o_proj"):
