@@ -251,6 +251,23 @@ def test_every_tabled_shape_resolves_to_a_valid_plan(fmt, shape):
                 assert need >= p.split_k * m * n * 4
 
 
+def test_tabled_whole_groups_follow_the_callers_group_size():
+    """A tabled whole-group count is meant for the table's n-tiles per
+    workgroup: with another workgroup shape it is scaled to keep the same
+    n-tiles whole (gate_up at M = 2: 512 groups of 4 tiles, or 256 of 8)."""
+    w = _w(n=34816, k=5120)
+    p = _plan(w, 2)
+    assert (p.waves_per_group, p.k_slices, p.split_k, p.whole_groups) == (4, 1, 4, 512)
+    p8 = _plan(w, 2, waves_per_group=8)
+    assert (p8.waves_per_group, p8.k_slices, p8.split_k, p8.whole_groups) == (8, 1, 4, 256)
+    p8s = _plan(w, 2, waves_per_group=8, epilogue=q.QPN_EPILOGUE_SWIGLU)
+    assert p8s.whole_groups == 256
+    # an explicit count is the caller's and is kept
+    assert _plan(w, 2, waves_per_group=8, split_k=4, whole_groups=100).whole_groups == 100
+    # the M = 1 entry already has 8-tile groups: nothing to scale
+    assert _plan(w, 1, waves_per_group=8).whole_groups == 256
+
+
 def test_valu_dot_plans_and_checks():
     """The VALU packed-dot path: m <= 4, plain epilogue, full stage, depth
     2..4; never chosen automatically."""
