@@ -204,7 +204,19 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  * epilogue. 0 in any shape field means "choose automatically".
  *   split_k          cut K into this many ranges over workgroups (their fp32
  *                    partials are added by the last workgroup to finish);
- *   waves_per_group  4 or 8 wavefronts per workgroup;
+ *   waves_per_group  4 or 8 wavefronts per workgroup; or 9 for the uneven
+ *                    grid: whole_groups workgroups share the n-tiles, one K
+ *                    slice each and no K split, the first (n-tiles mod
+ *                    whole_groups) of them taking one n-tile more than the
+ *                    others, at most 9. It takes NVFP4 weights,
+ *                    QPN_EPILOGUE_NONE or QPN_EPILOGUE_F32, the matrix
+ *                    cores, depth 2 or 3,
+ *                    k_slices and split_k 0 or 1, and 1 <= whole_groups <=
+ *                    n-tiles; else QPN_ERR_UNSUPPORTED. With whole_groups =
+ *                    the CU count every CU streams the same number of tiles
+ *                    to within one, without a split-K tail (qpn_gemm and
+ *                    qpn_gemm_f32 pick it for the 34816 x 5120 gate_up
+ *                    matrix from 9 rows on);
  *   depth            2, 3, 4, 6 or 8 units of the weight stream in flight per
  *                    wavefront;
  *   k_slices         1, 2, 4 or 8 (at most waves_per_group): wavefronts of
@@ -250,7 +262,8 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *                    one fp32 block sum per weight row instead of every
  *                    decoded weight. Other values return QPN_ERR_INVALID_ARG.
  * The result bits depend on split_k, whole_groups, k_slices, valu_dot and
- * block_columns (the summation order), not on the other fields.
+ * block_columns (the summation order), not on the other fields; the uneven
+ * grid sums like any launch with k_slices 1 and split_k 1.
  */
 typedef enum {
   QPN_EPILOGUE_NONE = 0,

@@ -153,7 +153,7 @@ qpn_status check_gemm(const void* x, const qpn_weight* w, const void* y, const f
   const qpn_status st = check_weight(w);
   if (st != QPN_OK) return st;
   if (m < 0 || m > QPN_MAX_M) return QPN_ERR_INVALID_ARG;
-  if (o.waves != 0 && o.waves != 4 && o.waves != 8) return QPN_ERR_INVALID_ARG;
+  if (o.waves != 0 && o.waves != 4 && o.waves != 8 && o.waves != kUnevenWaves) return QPN_ERR_INVALID_ARG;
   if (o.depth != 0 && o.depth != 2 && o.depth != 3 && o.depth != 4 && o.depth != 6 && o.depth != 8)
     return QPN_ERR_INVALID_ARG;
   if (o.k_slices != 0 && o.k_slices != 1 && o.k_slices != 2 && o.k_slices != 4 && o.k_slices != 8)

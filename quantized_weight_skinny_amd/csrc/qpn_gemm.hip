@@ -76,8 +76,12 @@ hipError_t launch_kernel(const GemmPlan& p, const void* x, const void* packed, c
   const int NT = static_cast<int>(ceil_div(n, kTileN));
   const int KU = static_cast<int>(ceil_div(k, kUnitK));
   const int groups = static_cast<int>(ceil_div(NT, WAVES / p.k_slices));
-  const int whole = p.split > 1 ? p.whole_groups : groups;  // groups that take all of K
+  // groups that take all of K (the uneven grid: its workgroups, all of them)
+  const int whole = WAVES == kUnevenWaves || p.split > 1 ? p.whole_groups : groups;
   const unsigned grid = static_cast<unsigned>(whole + (groups - whole) * (p.split > 1 ? p.split : 0));
+  if (WAVES == kUnevenWaves && (p.k_slices != 1 || p.split != 1 || whole < 1 || whole > NT ||
+                                ceil_div(NT, whole) > kUnevenWaves))
+    return hipErrorInvalidValue;
   // Dynamic LDS above the 64 KiB default must be allowed per kernel and device.
   static std::atomic<uint64_t> lds_allowed{0};
   const hipError_t attr = allow_dynamic_lds(
@@ -188,11 +192,44 @@ hipError_t launch_depth(const GemmPlan& p, const void* x, const void* packed, co
   }
 }
 
+// The uneven-group grid (NVFP4, fp16 or fp32 y, MFMA, depths 2 and 3).
+template <int EPI>
+hipError_t launch_uneven_e(const GemmPlan& p, const void* x, const void* packed, float tensor_scale, void* y,
+                           int m, int64_t n, int64_t k, hipStream_t stream) {
+  constexpr int W = kUnevenWaves;
+  const bool ring = p.x_stage == kStageRing;
+  if (ring && ring_pieces(W, 1, m) != 1) return hipErrorInvalidValue;
+  switch (p.depth) {
+    case 2:
+      return ring ? launch_kernel<kFmtNvfp4, W, 2, EPI, 1>(p, x, packed, nullptr, tensor_scale, y, nullptr, nullptr,
+                                                           m, n, k, stream)
+                  : launch_kernel<kFmtNvfp4, W, 2, EPI, 0>(p, x, packed, nullptr, tensor_scale, y, nullptr, nullptr,
+                                                           m, n, k, stream);
+    case 3:
+      return ring ? launch_kernel<kFmtNvfp4, W, 3, EPI, 1>(p, x, packed, nullptr, tensor_scale, y, nullptr, nullptr,
+                                                           m, n, k, stream)
+                  : launch_kernel<kFmtNvfp4, W, 3, EPI, 0>(p, x, packed, nullptr, tensor_scale, y, nullptr, nullptr,
+                                                           m, n, k, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_uneven(const GemmPlan& p, const void* x, const void* packed, float tensor_scale, void* y, int m,
+                         int64_t n, int64_t k, hipStream_t stream) {
+  if (p.dot_rows || p.block_cols) return hipErrorInvalidValue;
+  if (p.epilogue == kEpiNone) return launch_uneven_e<kEpiNone>(p, x, packed, tensor_scale, y, m, n, k, stream);
+  if (p.epilogue == kEpiF32) return launch_uneven_e<kEpiF32>(p, x, packed, tensor_scale, y, m, n, k, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int fmt, const GemmPlan& p, const void* x, const void* packed,
                        const float* row_scales, float tensor_scale, void* y, float* val, void* workspace,
                        int m, int64_t n, int64_t k, hipStream_t stream) {
+  if (p.waves == kUnevenWaves)
+    return fmt == kFmtNvfp4 ? launch_uneven(p, x, packed, tensor_scale, y, m, n, k, stream) : hipErrorInvalidValue;
   if (fmt == kFmtNvfp4) {
     return p.waves == 8 ? launch_depth<kFmtNvfp4, 8>(p, x, packed, row_scales, tensor_scale, y, val,
                                                       workspace, m, n, k, stream)

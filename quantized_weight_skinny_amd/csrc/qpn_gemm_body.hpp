@@ -326,6 +326,14 @@ __device__ __forceinline__ void gemm_body(
   static_assert(FUSE == 0 || (FUSE == 1 && EPI == kEpiSwiglu && DOT == 0) ||
                     (FUSE == 2 && EPI == kEpiNone && XP == 0 && DOT == 0),
                 "fused launch: a SwiGLU producer and a full-stage consumer");
+  // The uneven-group grid (one K slice, no K split, fp16 or fp32 y):
+  // `whole` is its workgroup count G, and workgroup b takes the NT / G or
+  // NT / G + 1 consecutive n-tiles from b * (NT / G) + min(b, NT % G), the
+  // larger count going to the first NT % G workgroups. Each CU then streams
+  // the same number of tiles to within one, with no split-K tail.
+  constexpr bool uneven = WAVES == kUnevenWaves;
+  static_assert(!uneven || ((EPI == kEpiNone || EPI == kEpiF32) && DOT == 0 && FUSE == 0),
+                "uneven grid: fp16 or fp32 y, MFMA");
   constexpr bool coherent_h = FUSE == 1;
   // The epilogue is a template parameter, so the plain kernels carry none of
   // the others: kEpiSwiglu writes h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:],
@@ -345,7 +353,15 @@ __device__ __forceinline__ void gemm_body(
   // units, one workgroup per range, range-major (all first ranges, then all
   // second ranges ...).
   int grp, s, S;
-  if (block < whole) {
+  int tile0 = 0, tiles = 0;  // the uneven grid's n-tiles of this workgroup
+  if (uneven) {
+    const int tmin = NT / whole, extra = NT - tmin * whole;
+    tile0 = block * tmin + min(block, extra);
+    tiles = tmin + (block < extra ? 1 : 0);
+    grp = block;
+    s = 0;
+    S = 1;
+  } else if (block < whole) {
     grp = block;
     s = 0;
     S = 1;
@@ -372,8 +388,8 @@ __device__ __forceinline__ void gemm_body(
   const int half_tn = TN / 2;
   const int NTh = NT / 2;
   const int pair = grp * half_tn + (tn < half_tn ? tn : tn - half_tn);
-  const int nt = swiglu ? (tn < half_tn ? pair : NTh + pair) : grp * TN + tn;
-  const bool active = swiglu ? pair < NTh : nt < NT;
+  const int nt = uneven ? tile0 + tn : swiglu ? (tn < half_tn ? pair : NTh + pair) : grp * TN + tn;
+  const bool active = uneven ? tn < tiles && nt < NT : swiglu ? pair < NTh : nt < NT;
   const uint32_t unit_stride = static_cast<uint32_t>(NT) * kBytes;
   // The weight stream is set up where the first weight units are issued:
   // after the activation loads, behind a scheduling barrier, so that its

@@ -22,6 +22,10 @@ namespace {
 //    wins on every matrix but one, at 4 it ties with the full stage);
 //  * no whole groups (all groups split alike): a balanced grid needs the
 //    shape's group count, and is only tabled where it was measured.
+// An uneven-group row (waves == kUnevenWaves) serves only calls that leave
+// the workgroup size, K slices, K split, whole groups and depth automatic
+// and ask for the fp16 or fp32 epilogue on the MFMA path; the others take
+// the next row of the shape.
 struct TunedLaunch {
   int fmt;
   int64_t n, k;
@@ -39,8 +43,16 @@ constexpr TunedLaunch kTuned[] = {
     // From 5 rows on, groups of 8 tiles (320 workgroups) beat groups of 4
     // (640): 19.80 against 19.94 us at M = 8, 19.50 against 19.99 with the
     // SwiGLU epilogue, 22.43 against 22.96 at M = 16 (ten alternated rounds).
+    // From 9 rows on the fp16 and fp32 epilogues take the uneven grid: 256
+    // workgroups of 9 wavefronts, 128 with 9 n-tiles and 128 with 8, no K
+    // split (M = 12: 20.06 / 20.32 against 21.12 / 21.57 us; M = 16: 20.34 /
+    // 21.08 / 21.21 against 22.11 / 22.43 / 22.44, three runs of six
+    // alternated rounds). At 1-5 rows it is slower (M = 1 19.11 against
+    // 18.14), at 6-8 level within the spread between runs.
     {kFmtNvfp4, 34816, 5120, 1, 8, 1, 4, 2, kStageRing, 256},
     {kFmtNvfp4, 34816, 5120, 2, 4, 1, 4, 2, kStageFull, 512},
+    {kFmtNvfp4, 34816, 5120, 8, 8, 1, 4, 2, kStageRing, 256},
+    {kFmtNvfp4, 34816, 5120, 16, kUnevenWaves, 1, 1, 2, kStageRing, 256},
     {kFmtNvfp4, 34816, 5120, 16, 8, 1, 4, 2, kStageRing, 256},
     // NVFP4 down 5120 x 17408 (at M = 3 and 4 the ring at depth 3 measured 12.43 / 12.48 us
     // against 12.45 / 12.68 for the full stage at depth 2, eight alternated rounds)
@@ -75,9 +87,16 @@ constexpr TunedLaunch kTuned[] = {
     {kFmtFp8, 5120, 17408, 16, 8, 2, 3, 2, kStageRing},
 };
 
-const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m) {
+// Whether an uneven-group row may serve this call (see TunedLaunch).
+bool uneven_row_ok(const LaunchOverride& o) {
+  return !o.waves && !o.k_slices && !o.split && !o.whole_groups && !o.depth &&
+         (o.epilogue == kEpiNone || o.epilogue == kEpiF32) && !o.valu_dot && o.block_cols != 1;
+}
+
+const TunedLaunch* find_tuned(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o) {
   for (const TunedLaunch& t : kTuned)
-    if (t.fmt == fmt && t.n == n && t.k == k && m <= t.m_max) return &t;
+    if (t.fmt == fmt && t.n == n && t.k == k && m <= t.m_max && (t.waves != kUnevenWaves || uneven_row_ok(o)))
+      return &t;
   return nullptr;
 }
 
@@ -121,7 +140,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   // M = 1 and 70.1 against 70.2 at M = 8).
   LaunchOverride w = o;
   int tuned_tn = 0;  // n-tiles per workgroup behind a tabled whole_groups (0: none tabled)
-  if (const TunedLaunch* t = find_tuned(fmt, n, k, m)) {
+  if (const TunedLaunch* t = find_tuned(fmt, n, k, m, o)) {
     if (!w.split) w.split = t->split;
     if (!w.waves) w.waves = t->waves;
     if (!w.k_slices) w.k_slices = t->k_slices;
@@ -133,8 +152,19 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
     }
   }
 
+  // The uneven-group grid: NVFP4, the fp16 or fp32 epilogue on the MFMA
+  // path, one K slice, no K split, at most kUnevenWaves n-tiles a workgroup.
+  const bool uneven = w.waves == kUnevenWaves;
+  if (uneven) {
+    if (fmt != kFmtNvfp4 || (o.epilogue != kEpiNone && o.epilogue != kEpiF32) || o.valu_dot || o.block_cols == 1)
+      return false;
+    if (w.k_slices > 1 || w.split > 1 || w.whole_groups <= 0 || w.whole_groups > NT) return false;
+    if (ceil_div(NT, w.whole_groups) > kUnevenWaves) return false;
+    if (w.depth && w.depth != 2 && w.depth != 3) return false;
+  }
+
   // K ranges over workgroups: as few as a full activation stage allows.
-  int64_t split = w.split > 0 ? w.split : (KU ? ceil_div(KU, max_ups) : 1);
+  int64_t split = uneven ? 1 : w.split > 0 ? w.split : (KU ? ceil_div(KU, max_ups) : 1);
   if (split > KU) split = KU ? KU : 1;
   if (split < 1) split = 1;
   const int64_t ups = KU ? ceil_div(KU, split) : 0;
@@ -143,7 +173,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   // n-tiles per workgroup first (from M), then as many K slices per n-tile
   // as the workgroup has room for and the K range supports.
   const int tn_target = m > 4 ? 4 : 2;
-  int ks = w.k_slices;
+  int ks = uneven ? 1 : w.k_slices;
   if (!ks) {
     const int ks_room = 8 / tn_target;
     ks = 1;
@@ -167,11 +197,11 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
       else return false;
     }
   }
-  if (waves != 4 && waves != 8) return false;
+  if (waves != 4 && waves != 8 && !uneven) return false;
   if (ks != 1 && ks != 2 && ks != 4 && ks != 8) return false;
   if (ks > waves) return false;
   if (o.epilogue == kEpiSwiglu && (waves / ks) % 2) return false;
-  const int depth = w.depth ? w.depth : 3;
+  const int depth = w.depth ? w.depth : uneven ? 2 : 3;
   if (depth != 2 && depth != 3 && depth != 4 && depth != 6 && depth != 8) return false;
   // The packed-dot path: the plain epilogue, a full stage, depths 2..4, and
   // at most 4 rows (its cost grows with M; the MFMA's does not).
@@ -216,7 +246,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   p->block_cols = bc_ok && o.block_cols == 1 ? 1 : 0;
 
   p->split = static_cast<int>(split);
-  p->whole_groups = split > 1 ? static_cast<int>(whole) : 0;
+  p->whole_groups = uneven ? w.whole_groups : split > 1 ? static_cast<int>(whole) : 0;
   p->waves = waves;
   p->depth = depth;
   p->k_slices = ks;
@@ -249,6 +279,7 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
 }
 
 int64_t gemm_grid(const GemmPlan& p, int64_t n) {
+  if (p.waves == kUnevenWaves) return p.whole_groups;
   const int64_t groups = ceil_div(ceil_div(n, kTileN), p.waves / p.k_slices);
   const int64_t whole = p.split > 1 ? p.whole_groups : groups;
   return whole + (groups - whole) * (p.split > 1 ? p.split : 0);

@@ -40,6 +40,11 @@ constexpr int kArgmaxSubs = 64;
 constexpr size_t kControlBytes = static_cast<size_t>(kArgmaxSubs) * kMaxM * sizeof(unsigned long long);
 constexpr int kFixupBatch = 8;  // split-K partials loaded together by the last workgroup
 
+// Workgroup size of the uneven-group grid: `whole_groups` workgroups share
+// the n-tiles, one K slice each and no K split; the first NT % whole_groups
+// of them take one n-tile more than the others, at most this many.
+constexpr int kUnevenWaves = 9;
+
 constexpr int kRowPad = 8;                  // fp16 pad per staged row (bank spread)
 constexpr int kRingSlots = 3;               // units per K slice in the ring stage
 constexpr int kRingRow = kUnitK + kRowPad;  // halves per row of a ring slot
@@ -57,7 +62,8 @@ struct LaunchOverride {
   int split = 0, waves = 0, depth = 0, k_slices = 0;  // 0 = automatic
   int epilogue = 0;  // 0: y[M, N]; 1: SwiGLU (h[M, N/2]); 2: greedy argmax per row; 3: fp32 y
   int x_stage = 0;   // 0 automatic; kStageFull; kStageRing
-  int whole_groups = 0;  // with split > 1: leading n-tile groups kept whole (not split)
+  int whole_groups = 0;  // with split > 1: leading n-tile groups kept whole (not split);
+                         // with waves == kUnevenWaves: the workgroups of the uneven grid
   int valu_dot = 0;      // 1: the VALU packed-dot path instead of the MFMA
   int block_cols = 0;    // one activation row, NVFP4: 1 on, 0 and 2 off
 };
@@ -71,7 +77,8 @@ struct GemmPlan {
   int depth;       // units of the weight stream each wavefront keeps in flight
   int epilogue;    // 0 y[M, N]; 1 h[M, N/2] = silu(y[:, :N/2]) * y[:, N/2:]; 2 argmax of each row; 3 fp32 y
   int x_stage;     // kStageFull or kStageRing
-  int whole_groups;  // split > 1: the first whole_groups groups of n-tiles take all of K
+  int whole_groups;  // split > 1: the first whole_groups groups of n-tiles take all of K;
+                     // waves == kUnevenWaves: the workgroups of the uneven grid
   int units_per_split;
   int lds_stride;  // halves per staged activation row (full stage)
   size_t lds_bytes;

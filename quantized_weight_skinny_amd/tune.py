@@ -39,6 +39,7 @@ SETTLE_MS = 30.0
 ROTATE_BYTES = 2_500_000_000  # as the benchmark: well past the memory-side cache
 MAX_COPIES = 256  # small weights rotate through at most this many copies
 FIELDS = ("waves", "k_slices", "split_k", "depth", "x_stage", "whole_groups")
+UNEVEN_WAVES = 9  # workgroup size of the planner's uneven-group grid
 
 
 def planner_weight(fmt, n, k):
@@ -57,9 +58,24 @@ def candidates(fmt, n, k, m, cus):
     """Every launch shape of the sweep grid that the planner accepts for this
     shape, resolved (so that equal launches appear once). With a K split, the
     groups are either all split or, where there are more groups than CUs, the
-    leading multiple of the CU count is kept whole (a balanced grid)."""
+    leading multiple of the CU count is kept whole (a balanced grid). For
+    NVFP4 the uneven grid of one workgroup per CU (UNEVEN_WAVES wavefronts)
+    joins in where the planner takes it."""
     w = planner_weight(fmt, n, k)
     seen, out = set(), []
+
+    def add(launch):
+        try:
+            p = qpn_gemm_plan(w, m, launch)
+        except QpnError:
+            return
+        kw = dict(waves=p.waves_per_group, k_slices=p.k_slices, split_k=p.split_k, depth=p.depth,
+                  x_stage=p.x_stage, whole_groups=p.whole_groups)
+        key = tuple(kw[f] for f in FIELDS)
+        if key not in seen:
+            seen.add(key)
+            out.append(kw)
+
     for waves, ks, split, depth, stage in itertools.product(
             (4, 8), (1, 2, 4, 8), (1, 2, 3, 4, 6), (2, 3, 4), (QPN_X_STAGE_FULL, QPN_X_STAGE_RING)):
         if ks > waves:
@@ -70,16 +86,9 @@ def candidates(fmt, n, k, m, cus):
         if split > 1 and groups > cus:
             wholes.append(groups // cus * cus)
         for whole in wholes:
-            try:
-                p = qpn_gemm_plan(w, m, make_launch(split, waves, depth, ks, x_stage=stage, whole_groups=whole))
-            except QpnError:
-                continue
-            kw = dict(waves=p.waves_per_group, k_slices=p.k_slices, split_k=p.split_k, depth=p.depth,
-                      x_stage=p.x_stage, whole_groups=p.whole_groups)
-            key = tuple(kw[f] for f in FIELDS)
-            if key not in seen:
-                seen.add(key)
-                out.append(kw)
+            add(make_launch(split, waves, depth, ks, x_stage=stage, whole_groups=whole))
+    for depth, stage in itertools.product((2, 3), (QPN_X_STAGE_FULL, QPN_X_STAGE_RING)):
+        add(make_launch(1, UNEVEN_WAVES, depth, 1, x_stage=stage, whole_groups=cus))
     return out
 
 
@@ -87,7 +96,8 @@ def table_entry(fmt, n, k, m_max, kw):
     """A kTuned line for this launch."""
     stage = "kStageRing" if kw["x_stage"] == QPN_X_STAGE_RING else "kStageFull"
     f = "kFmtNvfp4" if fmt == QPN_FMT_NVFP4 else "kFmtFp8"
-    return (f"{{{f}, {n}, {k}, {m_max}, {kw['waves']}, {kw['k_slices']}, {kw['split_k']}, {kw['depth']}, {stage}, "
+    waves = "kUnevenWaves" if kw["waves"] == UNEVEN_WAVES else kw["waves"]
+    return (f"{{{f}, {n}, {k}, {m_max}, {waves}, {kw['k_slices']}, {kw['split_k']}, {kw['depth']}, {stage}, "
             f"{kw['whole_groups']}}}")
 
 

@@ -54,7 +54,18 @@ void check_plan(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, c
   const int64_t NT = ceil_div(n, kTileN), KU = ceil_div(k, kUnitK);
   REQUIRE(fmt == kFmtNvfp4 || fmt == kFmtFp8);
   REQUIRE(m >= 1 && m <= kMaxM && n >= 1 && k >= 0);
-  REQUIRE(p.waves == 4 || p.waves == 8);
+  // The uneven-group grid: whole_groups workgroups of kUnevenWaves
+  // wavefronts share the n-tiles (at most kUnevenWaves each), NVFP4, fp16 or
+  // fp32 y on the MFMA path, one K slice, no split.
+  const bool uneven = p.waves == kUnevenWaves;
+  REQUIRE(p.waves == 4 || p.waves == 8 || uneven);
+  if (uneven) {
+    REQUIRE(fmt == kFmtNvfp4 && (p.epilogue == kEpiNone || p.epilogue == kEpiF32));
+    REQUIRE(p.k_slices == 1 && p.split == 1 && (p.depth == 2 || p.depth == 3));
+    REQUIRE(p.dot_rows == 0 && p.block_cols == 0);
+    REQUIRE(p.whole_groups >= 1 && p.whole_groups <= NT && ceil_div(NT, p.whole_groups) <= kUnevenWaves);
+    REQUIRE(gemm_grid(p, n) == p.whole_groups);
+  }
   REQUIRE(p.k_slices == 1 || p.k_slices == 2 || p.k_slices == 4 || p.k_slices == 8);
   REQUIRE(p.k_slices <= p.waves && p.waves % p.k_slices == 0);
   REQUIRE(p.depth == 2 || p.depth == 3 || p.depth == 4 || p.depth == 6 || p.depth == 8);
@@ -69,7 +80,7 @@ void check_plan(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, c
     REQUIRE(p.split == 1 && p.units_per_split == 0);
   }
   const int64_t groups = ceil_div(NT, p.waves / p.k_slices);
-  if (p.split == 1) REQUIRE(p.whole_groups == 0);
+  if (p.split == 1) REQUIRE(p.whole_groups == 0 || uneven);
   else REQUIRE(p.whole_groups >= 0 && p.whole_groups <= groups);
   // unit offsets inside a stream are 32-bit
   REQUIRE(NT * KU * (fmt == kFmtNvfp4 ? kNvUnitBytes : kF8UnitBytes) < (int64_t(1) << 31));
@@ -123,7 +134,7 @@ const int64_t kKs[] = {-256, -16, 0, 8, 16, 240, 256, 272, 1280, 4352, 5120, 174
                        int64_t(1) << 30, (int64_t(1) << 30) + 16, INT64_MAX - 15};
 const int kFmts[] = {0, kFmtNvfp4, kFmtFp8, 3};
 const int kSplits[] = {0, 0, 0, 1, 2, 3, 4, 6, 7, 100, -1};
-const int kWaves[] = {0, 0, 0, 4, 8, 2, -4, 16};
+const int kWaves[] = {0, 0, 0, 4, 8, 9, 2, -4, 16};
 const int kDepths[] = {0, 0, 0, 2, 3, 4, 6, 8, 5, -1};
 const int kSlices[] = {0, 0, 0, 1, 2, 4, 8, 3, 16};
 const int kEpis[] = {0, 0, 1, 2, 3, 4, -1};

@@ -224,14 +224,24 @@ def test_every_tabled_shape_resolves_to_a_valid_plan(fmt, shape):
     """For the shapes the launch table covers, every M = 1..16 (plain, SwiGLU
     where N allows, argmax) resolves to a launch within the kernel's limits:
     a full stage fits the 79 KiB LDS budget, a ring stays within its limits,
-    and the workspace covers the split."""
+    and the workspace covers the split. An uneven grid (9 wavefronts) takes
+    NVFP4, the fp16 or fp32 epilogue, one K slice and no split, and at most 9
+    n-tiles a workgroup."""
     n, k = shape
     w = q.make_weight(fmt, n, k, FAKE, 1.0, FAKE)
     ku, nt = -(-k // 256), -(-n // 16)
-    epis = [q.QPN_EPILOGUE_NONE, q.QPN_EPILOGUE_ARGMAX] + ([q.QPN_EPILOGUE_SWIGLU] if n % 32 == 0 else [])
+    epis = [q.QPN_EPILOGUE_NONE, q.QPN_EPILOGUE_F32, q.QPN_EPILOGUE_ARGMAX] + (
+        [q.QPN_EPILOGUE_SWIGLU] if n % 32 == 0 else [])
     for m in range(1, 17):
         for epi in epis:
             p = q.qpn_gemm_plan(w, m, q.make_launch(epilogue=epi))
+            if p.waves_per_group == 9:
+                assert fmt == q.QPN_FMT_NVFP4 and epi in (q.QPN_EPILOGUE_NONE, q.QPN_EPILOGUE_F32)
+                assert (p.k_slices, p.split_k) == (1, 1) and p.depth in (2, 3)
+                assert 1 <= p.whole_groups <= nt and -(-nt // p.whole_groups) <= 9
+                assert p.x_stage == q.QPN_X_STAGE_RING or 2 * m * (ku * 256 + 8) <= 79 * 1024
+                assert q.qpn_workspace_bytes_tuned(w, m, p) == 0
+                continue
             assert p.waves_per_group in (4, 8) and p.k_slices in (1, 2, 4, 8)
             assert p.waves_per_group % p.k_slices == 0 and p.depth in (2, 3, 4, 6, 8)
             ups = -(-ku // p.split_k)
@@ -249,6 +259,46 @@ def test_every_tabled_shape_resolves_to_a_valid_plan(fmt, shape):
             need = q.qpn_workspace_bytes_tuned(w, m, p)
             if p.split_k > 1:
                 assert need >= p.split_k * m * n * 4
+
+
+def test_uneven_grid_plans():
+    """The uneven-group grid: whole_groups workgroups of 9 wavefronts share
+    the n-tiles (the first NT mod G one more), one K slice, no split. The
+    planner takes it for gate_up from 9 rows on with the fp16 or fp32
+    epilogue and the shape fields left automatic; everything else keeps the
+    tabled split-K grid; explicit requests outside its limits are refused."""
+    w = _w(n=34816, k=5120)
+    ring = q.QPN_X_STAGE_RING
+    fields = lambda p: (p.waves_per_group, p.k_slices, p.split_k, p.depth, p.x_stage, p.whole_groups)  # noqa: E731
+    for m in (9, 12, 16):
+        assert fields(_plan(w, m)) == (9, 1, 1, 2, ring, 256)
+        assert fields(_plan(w, m, epilogue=q.QPN_EPILOGUE_F32)) == (9, 1, 1, 2, ring, 256)
+        assert fields(_plan(w, m, x_stage=ring)) == (9, 1, 1, 2, ring, 256)
+        assert _ws(w, m) == 0
+        for kw in (dict(epilogue=q.QPN_EPILOGUE_SWIGLU), dict(epilogue=q.QPN_EPILOGUE_ARGMAX), dict(depth=3),
+                   dict(waves_per_group=8), dict(k_slices=1), dict(split_k=4)):
+            p = _plan(w, m, **kw)
+            # (a caller's own split keeps all groups split, as on every shape)
+            whole = 0 if "split_k" in kw else 256
+            assert p.waves_per_group == 8 and p.split_k == 4 and p.whole_groups == whole, kw
+    for m in (1, 4, 8):
+        assert _plan(w, m).waves_per_group in (4, 8)
+    # explicit: NT = 37 n-tiles over 5 workgroups (8, 8, 7, 7, 7 tiles), ragged K
+    small = _w(n=16 * 37 - 5, k=304)
+    full = q.QPN_X_STAGE_FULL
+    assert fields(_plan(small, 3, split_k=1, waves_per_group=9, depth=2, k_slices=1, x_stage=full,
+                        whole_groups=5)) == (9, 1, 1, 2, full, 5)
+    assert fields(_plan(small, 16, waves_per_group=9, depth=3, x_stage=ring, whole_groups=37)) == \
+        (9, 1, 1, 3, ring, 37)
+    bad = q.QPN_ERR_UNSUPPORTED
+    for kw in (dict(k_slices=2), dict(split_k=2), dict(whole_groups=0), dict(whole_groups=4),
+               dict(whole_groups=38), dict(depth=4), dict(epilogue=q.QPN_EPILOGUE_ARGMAX),
+               dict(epilogue=q.QPN_EPILOGUE_SWIGLU), dict(valu_dot=1), dict(block_columns=1)):
+        args = dict(waves_per_group=9, whole_groups=5)
+        args.update(kw)
+        assert _plan(small, 1, **args) in (bad, q.QPN_ERR_INVALID_ARG), kw
+    assert _plan(_w(fmt=q.QPN_FMT_FP8_E4M3, n=16 * 37 - 5, k=304), 1, waves_per_group=9, whole_groups=5) == bad
+    assert _plan(small, 1, waves_per_group=7, whole_groups=5) in (bad, q.QPN_ERR_INVALID_ARG)
 
 
 def test_tabled_whole_groups_follow_the_callers_group_size():

@@ -122,6 +122,33 @@ def test_whole_groups_with_split_k(fmt, m, n, k, split, whole, waves, k_slices, 
     assert not to_host(ws[:(-(-n // 16)) * 4]).any()
 
 
+@pytest.mark.parametrize("m,n,k,groups,depth,stage", [
+    (1, 16 * 37 - 5, 304, 5, 2, 1),     # 37 n-tiles: 8, 8, 7, 7, 7; ragged N and K
+    (9, 16 * 37 - 5, 304, 5, 3, 2),
+    (16, 720, 1552, 5, 2, 2),           # 45 n-tiles, 9 each
+    (3, 720, 1552, 45, 3, 1),           # one n-tile each
+    (16, 1000, 5120, 7, 2, 2),          # 63 n-tiles, 9 each, 20 units of K
+    (8, 2000, 272, 16, 3, 2),           # 125 n-tiles: 13 workgroups of 8, 3 of 7
+    (2, 2000, 272, 125, 2, 1)])
+def test_uneven_grid(m, n, k, groups, depth, stage):
+    """The uneven-group grid (9 wavefronts, `groups` workgroups sharing the
+    n-tiles): every output within the bound, and the bits of the launch with
+    one K slice and no split at the same depth and stage (each n-tile is
+    summed over all of K by one wavefront in both), for fp16 and fp32 y."""
+    say("uneven grid", m, n, k, groups, depth, stage)
+    kw = dict(split_k=1, waves=9, k_slices=1, depth=depth, x_stage=stage, whole_groups=groups)
+    y = _parity("nvfp4", m, n, k, seed=900 + groups + m, **kw)
+    w = workloads.weights(n, k, 900 + groups + m)
+    x = to_dev(workloads.activations(m, k, 901 + groups + m))
+    pw, _ = gpu_quantize("nvfp4", to_dev(w))
+    ref = dict(split_k=1, waves=8, k_slices=1, depth=depth, x_stage=stage)
+    y8 = to_host(qt.gemm(x, pw, **ref))
+    assert np.array_equal(y.view(np.uint16), y8.view(np.uint16))
+    f9 = to_host(qt.gemm_f32(x, pw, **kw))
+    f8 = to_host(qt.gemm_f32(x, pw, **ref))
+    assert np.array_equal(f9.view(np.uint32), f8.view(np.uint32))
+
+
 def test_ring_stage_takes_a_k_range_the_full_stage_cannot():
     """down (17408) at 16 rows in one K range: 557 KB of activations per
     workgroup do not fit LDS, the 3-unit ring does."""
@@ -347,9 +374,10 @@ def test_empty_and_degenerate_shapes():
 
 
 # Every (format, matrix) the bench times, with every M the bench or the
-# 64-layer decode step (1, 2, 4, 8) runs it at.
+# 64-layer decode step (1, 2, 4, 8) runs it at (and gate_up at 9 rows, the
+# first that takes the uneven grid).
 FULL_M = {
-    ("nvfp4", "gate_up"): (1, 2, 4, 8, 16), ("nvfp4", "down"): (1, 2, 4, 8, 16), ("nvfp4", "qkv"): (1, 8),
+    ("nvfp4", "gate_up"): (1, 2, 4, 8, 9, 16), ("nvfp4", "down"): (1, 2, 4, 8, 16), ("nvfp4", "qkv"): (1, 8),
     ("nvfp4", "o_proj"): (1, 3, 8), ("nvfp4", "lm_head"): (1, 2, 4, 8), ("nvfp4", "gemv"): (1,),
     ("nvfp4", "qkv_tp4"): (1, 8), ("nvfp4", "o_proj_tp4"): (1, 8), ("nvfp4", "gate_up_tp4"): (1, 8),
     ("nvfp4", "down_tp4"): (1, 8), ("fp8", "qkv"): (1, 2, 4, 8), ("fp8", "down"): (1, 2, 4, 7, 8),
