@@ -175,8 +175,10 @@ qpn_status qpn_requantize_fp8_nvfp4(const uint8_t* fp8_codes_dev, const float* r
  * When K is split over several workgroups the workspace holds one arrival
  * counter per n-tile, an 8 KiB control block (the key slots of
  * qpn_gemm_argmax) and fp32 partial sums. The counters and the control block
- * sit at offsets that depend only on the weight, so one workspace (sized for
- * the largest m) serves calls with any m and epilogue. They must be zero
+ * sit at offsets that depend only on the weight, so one workspace serves
+ * calls with any m and epilogue once it is as large as the largest need
+ * among them (this and qpn_workspace_bytes_tuned per call; the need is not
+ * monotonic in m: a launch without a K split needs none). They must be zero
  * before the first call that uses the workspace (allocate it zeroed); every
  * call leaves them zero again. Calls that run at the same time must not
  * share a workspace. */
@@ -216,7 +218,7 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *                    the CU count every CU streams the same number of tiles
  *                    to within one, without a split-K tail (qpn_gemm and
  *                    qpn_gemm_f32 pick it for the 34816 x 5120 gate_up
- *                    matrix from 9 rows on);
+ *                    matrix from 8 rows on);
  *   depth            2, 3, 4, 6 or 8 units of the weight stream in flight per
  *                    wavefront;
  *   k_slices         1, 2, 4 or 8 (at most waves_per_group): wavefronts of

@@ -43,15 +43,15 @@ constexpr TunedLaunch kTuned[] = {
     // From 5 rows on, groups of 8 tiles (320 workgroups) beat groups of 4
     // (640): 19.80 against 19.94 us at M = 8, 19.50 against 19.99 with the
     // SwiGLU epilogue, 22.43 against 22.96 at M = 16 (ten alternated rounds).
-    // From 9 rows on the fp16 and fp32 epilogues take the uneven grid: 256
+    // From 8 rows on the fp16 and fp32 epilogues take the uneven grid: 256
     // workgroups of 9 wavefronts, 128 with 9 n-tiles and 128 with 8, no K
-    // split (M = 12: 20.06 / 20.32 against 21.12 / 21.57 us; M = 16: 20.34 /
-    // 21.08 / 21.21 against 22.11 / 22.43 / 22.44, three runs of six
-    // alternated rounds). At 1-5 rows it is slower (M = 1 19.11 against
-    // 18.14), at 6-8 level within the spread between runs.
+    // split (M = 8: 19.43 against 19.80 us, median of twelve alternated
+    // rounds, -1.6% over five runs; M = 12: 20.06 / 20.32 against 21.12 /
+    // 21.57; M = 16: 20.34 / 21.08 / 21.21 against 22.11 / 22.43 / 22.44).
+    // At 1-5 rows it is slower (M = 1 19.11 against 18.14), at 6-7 level.
     {kFmtNvfp4, 34816, 5120, 1, 8, 1, 4, 2, kStageRing, 256},
     {kFmtNvfp4, 34816, 5120, 2, 4, 1, 4, 2, kStageFull, 512},
-    {kFmtNvfp4, 34816, 5120, 8, 8, 1, 4, 2, kStageRing, 256},
+    {kFmtNvfp4, 34816, 5120, 7, 8, 1, 4, 2, kStageRing, 256},
     {kFmtNvfp4, 34816, 5120, 16, kUnevenWaves, 1, 1, 2, kStageRing, 256},
     {kFmtNvfp4, 34816, 5120, 16, 8, 1, 4, 2, kStageRing, 256},
     // NVFP4 down 5120 x 17408 (at M = 3 and 4 the ring at depth 3 measured 12.43 / 12.48 us

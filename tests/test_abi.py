@@ -264,13 +264,13 @@ def test_every_tabled_shape_resolves_to_a_valid_plan(fmt, shape):
 def test_uneven_grid_plans():
     """The uneven-group grid: whole_groups workgroups of 9 wavefronts share
     the n-tiles (the first NT mod G one more), one K slice, no split. The
-    planner takes it for gate_up from 9 rows on with the fp16 or fp32
+    planner takes it for gate_up from 8 rows on with the fp16 or fp32
     epilogue and the shape fields left automatic; everything else keeps the
     tabled split-K grid; explicit requests outside its limits are refused."""
     w = _w(n=34816, k=5120)
     ring = q.QPN_X_STAGE_RING
     fields = lambda p: (p.waves_per_group, p.k_slices, p.split_k, p.depth, p.x_stage, p.whole_groups)  # noqa: E731
-    for m in (9, 12, 16):
+    for m in (8, 9, 12, 16):
         assert fields(_plan(w, m)) == (9, 1, 1, 2, ring, 256)
         assert fields(_plan(w, m, epilogue=q.QPN_EPILOGUE_F32)) == (9, 1, 1, 2, ring, 256)
         assert fields(_plan(w, m, x_stage=ring)) == (9, 1, 1, 2, ring, 256)
@@ -281,7 +281,7 @@ def test_uneven_grid_plans():
             # (a caller's own split keeps all groups split, as on every shape)
             whole = 0 if "split_k" in kw else 256
             assert p.waves_per_group == 8 and p.split_k == 4 and p.whole_groups == whole, kw
-    for m in (1, 4, 8):
+    for m in (1, 4, 7):
         assert _plan(w, m).waves_per_group in (4, 8)
     # explicit: NT = 37 n-tiles over 5 workgroups (8, 8, 7, 7, 7 tiles), ragged K
     small = _w(n=16 * 37 - 5, k=304)
@@ -426,9 +426,12 @@ def test_swiglu_epilogue_plans_and_checks():
     for m in (1, 2, 4, 8, 16):
         p = q.qpn_gemm_plan(_w(n=1056, k=2304), m, sw)
         assert (p.waves_per_group // p.k_slices) % 2 == 0
-    # the split (and so the workspace) is the plain GEMM's
+    # up to 7 rows the split (and so the workspace) is the plain GEMM's; from
+    # 8 rows on the plain GEMM takes the uneven grid and needs none, while
+    # SwiGLU keeps its split tail and its own workspace
     w = _w(n=34816, k=5120)
-    assert q.qpn_workspace_bytes_tuned(w, 8, sw) == q.qpn_workspace_bytes(w, 8)
+    assert q.qpn_workspace_bytes_tuned(w, 4, sw) == q.qpn_workspace_bytes(w, 4) > 0
+    assert q.qpn_workspace_bytes(w, 8) == 0 and q.qpn_workspace_bytes_tuned(w, 8, sw) > 0
     # N must split into two halves of whole 16-row tiles
     assert q.lib().qpn_gemm_swiglu(FAKE, ctypes.byref(_w(n=48, k=256)), FAKE, 1, None, 0, None) == \
         q.QPN_ERR_INVALID_ARG

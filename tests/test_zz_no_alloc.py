@@ -49,11 +49,11 @@ def _weight(fmt, name, wl="no_alloc"):
 
 
 def test_noalloc_matches_the_workspace_entry_point_on_calls_in_a_row():
-    # largest first: gate_up at 8 rows (split tail partials, 4.5 MB of
+    # largest first: gate_up at 4 rows (split tail partials, 2.2 MB of
     # scratch), then down at 8 rows (split 3), then FP8 down at 2 rows, then
     # launches with no split at all (gate_up at 16 rows on the uneven grid,
     # the output head at one row)
-    cases = [("nvfp4", "gate_up", 8), ("nvfp4", "down", 8), ("fp8", "down", 2), ("nvfp4", "gate_up", 16),
+    cases = [("nvfp4", "gate_up", 4), ("nvfp4", "down", 8), ("fp8", "down", 2), ("nvfp4", "gate_up", 16),
              ("nvfp4", "lm_head", 1)]
     needs = []
     for fmt, name, m in cases:
