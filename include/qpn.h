@@ -218,7 +218,7 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *                    the CU count every CU streams the same number of tiles
  *                    to within one, without a split-K tail (qpn_gemm and
  *                    qpn_gemm_f32 pick it for the 34816 x 5120 gate_up
- *                    matrix from 8 rows on);
+ *                    matrix from 9 rows on);
  *   depth            2, 3, 4, 6 or 8 units of the weight stream in flight per
  *                    wavefront;
  *   k_slices         1, 2, 4 or 8 (at most waves_per_group): wavefronts of

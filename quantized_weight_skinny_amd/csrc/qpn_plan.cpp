@@ -36,24 +36,27 @@ struct TunedLaunch {
 };
 
 constexpr TunedLaunch kTuned[] = {
-    // NVFP4 gate_up 34816 x 5120: 2176 n-tiles. Whole groups of 8 (or 4)
-    // tiles fill the 256 CUs evenly (256 or 512 groups); the last 16 (32)
-    // groups split K four ways, a short tail of small workgroups. At M = 2
-    // the full stage beats the ring (18.5 against 19.4 us, alternated runs).
-    // From 5 rows on, groups of 8 tiles (320 workgroups) beat groups of 4
-    // (640): 19.80 against 19.94 us at M = 8, 19.50 against 19.99 with the
-    // SwiGLU epilogue, 22.43 against 22.96 at M = 16 (ten alternated rounds).
-    // From 8 rows on the fp16 and fp32 epilogues take the uneven grid: 256
-    // workgroups of 9 wavefronts, 128 with 9 n-tiles and 128 with 8, no K
-    // split (M = 8: 19.43 against 19.80 us, median of twelve alternated
-    // rounds, -1.6% over five runs; M = 12: 20.06 / 20.32 against 21.12 /
-    // 21.57; M = 16: 20.34 / 21.08 / 21.21 against 22.11 / 22.43 / 22.44).
-    // At 1-5 rows it is slower (M = 1 19.11 against 18.14), at 6-7 level.
-    {kFmtNvfp4, 34816, 5120, 1, 8, 1, 4, 2, kStageRing, 256},
-    {kFmtNvfp4, 34816, 5120, 2, 4, 1, 4, 2, kStageFull, 512},
-    {kFmtNvfp4, 34816, 5120, 7, 8, 1, 4, 2, kStageRing, 256},
+    // NVFP4 gate_up 34816 x 5120: 2176 n-tiles. 256 whole groups of 8 tiles
+    // fill the 256 CUs evenly; the last 16 groups split K, a short tail of
+    // small workgroups that share CUs with whole groups. Up to 2 rows the
+    // tail is split four ways; from 3 rows five (4 units a range, so the
+    // busiest CU streams 192 tile-units instead of 200): M = 6 18.61
+    // against 19.23 us, M = 8 18.87 / 18.98 / 19.03 against 19.34 / 19.57 /
+    // 19.66, M = 4 18.02 / 18.23 against 18.21 / 18.50 (three machines, ten
+    // or twelve alternated rounds); at 1 row no better (17.64 / 17.77 /
+    // 18.07 against 17.90 / 17.95 / 17.96), with SwiGLU worse (18.67 / 19.02
+    // against 18.53 / 18.71). At 2 rows this grid beats groups of 4 tiles
+    // with a full stage (18.05 against 18.51 us). From 9 rows on the fp16
+    // and fp32 epilogues take the uneven grid: 256 workgroups of 9
+    // wavefronts, 128 with 9 n-tiles and 128 with 8, no K split (M = 12
+    // 19.80 against 20.60 for the five-way tail, M = 16 20.53 against 22.03;
+    // against the four-way tail M = 9 18.67 / 19.74, M = 16 19.67 / 22.20).
+    // At 8 rows it ties with the five-way tail (18.99 / 18.64 against 18.98
+    // / 18.87), below that it is slower (M = 1 18.52 against 17.95).
+    {kFmtNvfp4, 34816, 5120, 2, 8, 1, 4, 2, kStageRing, 256},
+    {kFmtNvfp4, 34816, 5120, 8, 8, 1, 5, 2, kStageRing, 256},
     {kFmtNvfp4, 34816, 5120, 16, kUnevenWaves, 1, 1, 2, kStageRing, 256},
-    {kFmtNvfp4, 34816, 5120, 16, 8, 1, 4, 2, kStageRing, 256},
+    {kFmtNvfp4, 34816, 5120, 16, 8, 1, 5, 2, kStageRing, 256},
     // NVFP4 down 5120 x 17408 (at M = 3 and 4 the ring at depth 3 measured 12.43 / 12.48 us
     // against 12.45 / 12.68 for the full stage at depth 2, eight alternated rounds)
     {kFmtNvfp4, 5120, 17408, 2, 8, 4, 1, 3}, {kFmtNvfp4, 5120, 17408, 4, 8, 2, 3, 3, kStageRing},

@@ -264,13 +264,13 @@ def test_every_tabled_shape_resolves_to_a_valid_plan(fmt, shape):
 def test_uneven_grid_plans():
     """The uneven-group grid: whole_groups workgroups of 9 wavefronts share
     the n-tiles (the first NT mod G one more), one K slice, no split. The
-    planner takes it for gate_up from 8 rows on with the fp16 or fp32
+    planner takes it for gate_up from 9 rows on with the fp16 or fp32
     epilogue and the shape fields left automatic; everything else keeps the
     tabled split-K grid; explicit requests outside its limits are refused."""
     w = _w(n=34816, k=5120)
     ring = q.QPN_X_STAGE_RING
     fields = lambda p: (p.waves_per_group, p.k_slices, p.split_k, p.depth, p.x_stage, p.whole_groups)  # noqa: E731
-    for m in (8, 9, 12, 16):
+    for m in (9, 12, 16):
         assert fields(_plan(w, m)) == (9, 1, 1, 2, ring, 256)
         assert fields(_plan(w, m, epilogue=q.QPN_EPILOGUE_F32)) == (9, 1, 1, 2, ring, 256)
         assert fields(_plan(w, m, x_stage=ring)) == (9, 1, 1, 2, ring, 256)
@@ -279,10 +279,10 @@ def test_uneven_grid_plans():
                    dict(waves_per_group=8), dict(k_slices=1), dict(split_k=4)):
             p = _plan(w, m, **kw)
             # (a caller's own split keeps all groups split, as on every shape)
-            whole = 0 if "split_k" in kw else 256
-            assert p.waves_per_group == 8 and p.split_k == 4 and p.whole_groups == whole, kw
-    for m in (1, 4, 7):
-        assert _plan(w, m).waves_per_group in (4, 8)
+            whole, split = (0, 4) if "split_k" in kw else (256, 5)
+            assert p.waves_per_group == 8 and p.split_k == split and p.whole_groups == whole, kw
+    for m in (1, 4, 8):
+        assert _plan(w, m).waves_per_group == 8
     # explicit: NT = 37 n-tiles over 5 workgroups (8, 8, 7, 7, 7 tiles), ragged K
     small = _w(n=16 * 37 - 5, k=304)
     full = q.QPN_X_STAGE_FULL
@@ -304,17 +304,19 @@ def test_uneven_grid_plans():
 def test_tabled_whole_groups_follow_the_callers_group_size():
     """A tabled whole-group count is meant for the table's n-tiles per
     workgroup: with another workgroup shape it is scaled to keep the same
-    n-tiles whole (gate_up at M = 2: 512 groups of 4 tiles, or 256 of 8)."""
+    n-tiles whole (gate_up at M = 2: 256 groups of 8 tiles, or 512 of 4)."""
     w = _w(n=34816, k=5120)
     p = _plan(w, 2)
-    assert (p.waves_per_group, p.k_slices, p.split_k, p.whole_groups) == (4, 1, 4, 512)
-    p8 = _plan(w, 2, waves_per_group=8)
-    assert (p8.waves_per_group, p8.k_slices, p8.split_k, p8.whole_groups) == (8, 1, 4, 256)
-    p8s = _plan(w, 2, waves_per_group=8, epilogue=q.QPN_EPILOGUE_SWIGLU)
-    assert p8s.whole_groups == 256
+    assert (p.waves_per_group, p.k_slices, p.split_k, p.whole_groups) == (8, 1, 4, 256)
+    p4 = _plan(w, 2, waves_per_group=4)
+    assert (p4.waves_per_group, p4.k_slices, p4.split_k, p4.whole_groups) == (4, 1, 4, 512)
+    p4s = _plan(w, 2, waves_per_group=4, epilogue=q.QPN_EPILOGUE_SWIGLU)
+    assert p4s.whole_groups == 512
+    # two K slices of 8 wavefronts: groups of 4 tiles again
+    assert _plan(w, 2, k_slices=2).whole_groups == 512
     # an explicit count is the caller's and is kept
-    assert _plan(w, 2, waves_per_group=8, split_k=4, whole_groups=100).whole_groups == 100
-    # the M = 1 entry already has 8-tile groups: nothing to scale
+    assert _plan(w, 2, waves_per_group=4, split_k=4, whole_groups=100).whole_groups == 100
+    # the entry already has 8-tile groups: nothing to scale
     assert _plan(w, 1, waves_per_group=8).whole_groups == 256
 
 
@@ -426,12 +428,12 @@ def test_swiglu_epilogue_plans_and_checks():
     for m in (1, 2, 4, 8, 16):
         p = q.qpn_gemm_plan(_w(n=1056, k=2304), m, sw)
         assert (p.waves_per_group // p.k_slices) % 2 == 0
-    # up to 7 rows the split (and so the workspace) is the plain GEMM's; from
-    # 8 rows on the plain GEMM takes the uneven grid and needs none, while
+    # up to 8 rows the split (and so the workspace) is the plain GEMM's; from
+    # 9 rows on the plain GEMM takes the uneven grid and needs none, while
     # SwiGLU keeps its split tail and its own workspace
     w = _w(n=34816, k=5120)
     assert q.qpn_workspace_bytes_tuned(w, 4, sw) == q.qpn_workspace_bytes(w, 4) > 0
-    assert q.qpn_workspace_bytes(w, 8) == 0 and q.qpn_workspace_bytes_tuned(w, 8, sw) > 0
+    assert q.qpn_workspace_bytes(w, 9) == 0 and q.qpn_workspace_bytes_tuned(w, 9, sw) > 0
     # N must split into two halves of whole 16-row tiles
     assert q.lib().qpn_gemm_swiglu(FAKE, ctypes.byref(_w(n=48, k=256)), FAKE, 1, None, 0, None) == \
         q.QPN_ERR_INVALID_ARG

@@ -374,8 +374,8 @@ def test_empty_and_degenerate_shapes():
 
 
 # Every (format, matrix) the bench times, with every M the bench or the
-# 64-layer decode step (1, 2, 4, 8) runs it at (and gate_up at 9 rows: from 8
-# rows on it takes the uneven grid).
+# 64-layer decode step (1, 2, 4, 8) runs it at (and gate_up at 9 rows, the
+# first that takes the uneven grid).
 FULL_M = {
     ("nvfp4", "gate_up"): (1, 2, 4, 8, 9, 16), ("nvfp4", "down"): (1, 2, 4, 8, 16), ("nvfp4", "qkv"): (1, 8),
     ("nvfp4", "o_proj"): (1, 3, 8), ("nvfp4", "lm_head"): (1, 2, 4, 8), ("nvfp4", "gemv"): (1,),
