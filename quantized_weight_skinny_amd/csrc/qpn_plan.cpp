@@ -143,7 +143,11 @@ bool plan_gemm(int fmt, int64_t n, int64_t k, int m, const LaunchOverride& o, Ge
   // M = 1 and 70.1 against 70.2 at M = 8).
   LaunchOverride w = o;
   int tuned_tn = 0;  // n-tiles per workgroup behind a tabled whole_groups (0: none tabled)
-  if (const TunedLaunch* t = find_tuned(fmt, n, k, m, o)) {
+  const TunedLaunch* t = find_tuned(fmt, n, k, m, o);
+  // An explicit request for the uneven grid takes nothing from a row of
+  // another grid (its K split and slices do not apply there).
+  if (t && o.waves == kUnevenWaves && t->waves != kUnevenWaves) t = nullptr;
+  if (t) {
     if (!w.split) w.split = t->split;
     if (!w.waves) w.waves = t->waves;
     if (!w.k_slices) w.k_slices = t->k_slices;

@@ -283,9 +283,14 @@ def test_uneven_grid_plans():
             assert p.waves_per_group == 8 and p.split_k == split and p.whole_groups == whole, kw
     for m in (1, 4, 8):
         assert _plan(w, m).waves_per_group == 8
+    # an explicit request on a tabled shape takes nothing from the rows of
+    # the balanced grid (no K split, one slice, depth 2, the stage by M)
+    full = q.QPN_X_STAGE_FULL
+    assert fields(_plan(w, 1, waves_per_group=9, whole_groups=256)) == (9, 1, 1, 2, full, 256)
+    assert fields(_plan(w, 8, waves_per_group=9, whole_groups=256)) == (9, 1, 1, 2, ring, 256)
+    assert fields(_plan(w, 16, waves_per_group=9, whole_groups=512, depth=3)) == (9, 1, 1, 3, ring, 512)
     # explicit: NT = 37 n-tiles over 5 workgroups (8, 8, 7, 7, 7 tiles), ragged K
     small = _w(n=16 * 37 - 5, k=304)
-    full = q.QPN_X_STAGE_FULL
     assert fields(_plan(small, 3, split_k=1, waves_per_group=9, depth=2, k_slices=1, x_stage=full,
                         whole_groups=5)) == (9, 1, 1, 2, full, 5)
     assert fields(_plan(small, 16, waves_per_group=9, depth=3, x_stage=ring, whole_groups=37)) == \
