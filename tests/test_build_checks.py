@@ -1,7 +1,8 @@
 """Build-level checks on the CPU: the library's sources compile warning-free
 with -Wall -Wextra on both the host and the gfx950 pass, the device code holds
-no M0 write but the LDS-DMA staging sequence, no packed fp32 arithmetic and no
-store through the scalar data cache, and the launch planner and the C ABI's
+no M0 write but the LDS-DMA staging sequence, no packed fp32 arithmetic, no
+store through the scalar data cache and no scratch memory or register spills,
+and the launch planner and the C ABI's
 argument checks run clean under AddressSanitizer and UndefinedBehaviorSanitizer
 (a plain host build with g++, driven by tests/host/check_plan.cpp).
 """
@@ -98,6 +99,19 @@ def test_device_code_no_scalar_stores(device_asm):
     for src, text in device_asm.items():
         hits = [s for s in _instructions(text) if pat.search(s)]
         assert not hits, f"{src}: writes through the scalar data cache: {hits[:5]}"
+
+
+@needs_hipcc
+def test_device_code_no_scratch_or_spills(device_asm):
+    # every kernel keeps its state in registers and LDS: no private segment
+    # (scratch memory per lane) and no register spills
+    kernels = 0
+    for src, text in device_asm.items():
+        for key in (".private_segment_fixed_size", ".sgpr_spill_count", ".vgpr_spill_count"):
+            vals = re.findall(re.escape(key) + r":\s+(\d+)", text)
+            assert all(v == "0" for v in vals), (src, key, sorted(set(vals)))
+        kernels += len(re.findall(r"\.private_segment_fixed_size:", text))
+    assert kernels > 100
 
 
 @needs_hipcc
