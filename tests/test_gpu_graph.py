@@ -39,6 +39,32 @@ def test_graph_replay_matches_eager(fmt, n, k, m):
         assert not to_host(ws[:64]).any()
 
 
+@pytest.mark.parametrize("stage", [1, 2])
+def test_graph_replay_uneven_grid(stage):
+    """The uneven-group grid (9 wavefronts, 5 workgroups sharing 45 n-tiles)
+    captured in a graph: every replay gives the eager bits."""
+    say("graph replay uneven", stage)
+    n, k, m = 720, 1552, 12 if stage == 2 else 3
+    w = workloads.weights(n, k, 51)
+    pw, _ = gpu_quantize("nvfp4", to_dev(w))
+    x = to_dev(workloads.activations(m, k, 52))
+    y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+    kw = dict(split_k=1, waves=9, k_slices=1, depth=2, x_stage=stage, whole_groups=5)
+    assert qt.new_workspace(pw, m, **kw) is None
+    qt.gemm(x, pw, out=y, **kw)
+    eager = to_host(y).copy()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qt.gemm(x, pw, out=y, **kw)
+    for i in range(5):
+        y.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(y).view(np.uint16), eager.view(np.uint16)), i
+
+
 @pytest.mark.parametrize("split", [0, 3])
 def test_graph_replay_fused_epilogues(split):
     """The SwiGLU and greedy-argmax epilogues captured together in one graph
