@@ -244,7 +244,9 @@ qpn_status qpn_gemm(const void* x_dev, const qpn_weight* w, void* y_dev, int32_t
  *                    tuned value when split_k is automatic, else all split.
  *                    Whole groups first, then the split ones' ranges: a grid
  *                    that fills the CUs evenly and leaves a short tail of
- *                    small workgroups. A full stage must hold all of K;
+ *                    small workgroups. A full stage must hold all of K.
+ *                    With waves_per_group = 9 it is instead the workgroup
+ *                    count of the uneven grid (required there);
  *   valu_dot         0: the matrix cores (v_mfma_f32_16x16x32_f16, the
  *                    default); 1: the VALU packed-dot path instead
  *                    (v_dot2c_f32_f16: each lane adds its row's weight pairs
